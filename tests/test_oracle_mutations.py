@@ -1,0 +1,167 @@
+"""Plant plausible mistakes in a private copy of the oracle and show that the
+pins catch every one of them (CPU only; the real oracle is never modified)."""
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+import oracle_pins
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                          "oracle", "qsa_oracle.py")
+
+
+def fresh_oracle():
+    spec = importlib.util.spec_from_file_location("oracle_mutant", ORACLE_SRC)
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+def _m_tie_higher_index(m):
+    def select_blocks(scores, k=m.TOPK):
+        s = np.asarray(scores, np.float32).astype(np.float64)
+        nf = s.shape[0]
+        if nf <= k:
+            return np.arange(nf)
+        order = np.lexsort((-np.arange(nf), -s))
+        return np.sort(order[:k])
+    m.select_blocks = select_blocks
+
+
+def _m_unsorted_output(m):
+    def select_blocks(scores, k=m.TOPK):
+        s = np.asarray(scores, np.float32).astype(np.float64)
+        nf = s.shape[0]
+        if nf <= k:
+            return np.arange(nf)
+        return np.lexsort((np.arange(nf), -s))[:k]
+    m.select_blocks = select_blocks
+
+
+def _m_bottom_k(m):
+    def select_blocks(scores, k=m.TOPK):
+        s = np.asarray(scores, np.float32).astype(np.float64)
+        nf = s.shape[0]
+        if nf <= k:
+            return np.arange(nf)
+        return np.sort(np.lexsort((np.arange(nf), s))[:k])
+    m.select_blocks = select_blocks
+
+
+def _m_drop_partial(m):
+    orig = m.build_positions
+    def build_positions(sel, L, kv_start, k=m.TOPK):
+        return orig(sel, L - L % 4, kv_start, k)
+    m.build_positions = build_positions
+
+
+def _m_no_kv_offset(m):
+    orig = m.build_positions
+    def build_positions(sel, L, kv_start, k=m.TOPK):
+        return orig(sel, L, 0, k)
+    m.build_positions = build_positions
+
+
+def _m_all_queries_full_length(m):
+    m.query_length = lambda seq_len, nq, j: int(seq_len)
+
+
+def _m_causal_off_by_one(m):
+    m.query_length = lambda seq_len, nq, j: int(seq_len) - int(nq) + int(j)
+
+
+def _m_ignore_scale(m):
+    orig = m.sparse_attention
+    m.sparse_attention = lambda qh, kr, vr, sm: orig(qh, kr, vr, 1.0)
+
+
+def _m_gqa_modulo(m):
+    def sparse_attention(q_heads, k_rows, v_rows, sm_scale):
+        Hq, d = q_heads.shape
+        Hkv = k_rows.shape[1]
+        out = np.empty((Hq, d))
+        for h in range(Hq):
+            g = h % Hkv
+            z = (k_rows[:, g, :] @ q_heads[h]) * sm_scale
+            p = np.exp(z - z.max())
+            out[h] = (p @ v_rows[:, g, :]) / p.sum()
+        return out
+    m.sparse_attention = sparse_attention
+
+
+def _m_fp8_bias8(m):
+    def fp8(codes):
+        c = np.asarray(codes, np.uint8).astype(np.int64)
+        s, e, mm = (c >> 7) & 1, (c >> 3) & 15, c & 7
+        mag = np.where(e == 0, np.ldexp(mm / 8.0, -7), np.ldexp(1.0 + mm / 8.0, e - 8))
+        mag = np.where((e == 15) & (mm == 7), np.nan, mag)
+        return np.where(s == 1, -mag, mag)
+    m.fp8_e4m3fn_to_f64 = fp8
+
+
+def _m_fp8_no_subnormals(m):
+    def fp8(codes):
+        c = np.asarray(codes, np.uint8).astype(np.int64)
+        s, e, mm = (c >> 7) & 1, (c >> 3) & 15, c & 7
+        mag = np.ldexp(1.0 + mm / 8.0, e - 7)
+        mag = np.where((e == 15) & (mm == 7), np.nan, mag)
+        return np.where(s == 1, -mag, mag)
+    m.fp8_e4m3fn_to_f64 = fp8
+
+
+def _m_swap_kv_scales(m):
+    orig = m.decode
+    def decode(*a, **kw):
+        a = list(a)
+        a[10], a[11] = a[11], a[10]
+        return orig(*a, **kw)
+    m.decode = decode
+
+
+def _m_score_sign(m):
+    orig = m.block_scores
+    m.block_scores = lambda iq, keys: -orig(iq, keys)
+
+
+def _m_score_in_bf16(m):
+    orig = m.block_scores
+    def block_scores(iq, keys):
+        s = orig(iq, keys)
+        u = s.view(np.uint32) & np.uint32(0xFFFF0000)
+        return u.view(np.float32)
+    m.block_scores = block_scores
+
+
+def _m_ignore_blk_start(m):
+    orig = m.decode
+    def decode(q_start, seq_len, kv_start, blk_start, *a, **kw):
+        return orig(q_start, seq_len, kv_start, np.zeros_like(blk_start), *a, **kw)
+    m.decode = decode
+
+
+def _m_sel_pad_keeps_k(m):
+    orig = m.select_blocks
+    def select_blocks(scores, k=m.TOPK):
+        got = orig(scores, k)
+        return got[:-1] if got.shape[0] > 1 else got
+    m.select_blocks = select_blocks
+
+
+MUTANTS = [_m_tie_higher_index, _m_unsorted_output, _m_bottom_k, _m_drop_partial, _m_no_kv_offset,
+           _m_all_queries_full_length, _m_causal_off_by_one, _m_ignore_scale, _m_gqa_modulo,
+           _m_fp8_bias8, _m_fp8_no_subnormals, _m_swap_kv_scales, _m_score_sign, _m_score_in_bf16,
+           _m_ignore_blk_start, _m_sel_pad_keeps_k]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__[3:])
+def test_pins_catch_mutant(mutant):
+    m = fresh_oracle()
+    mutant(m)
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(m)
+        except AssertionError:
+            return
+    pytest.fail(f"no pin caught mutant {mutant.__name__}")
