@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused QSA decode step on one MI355X.
+
+One step = one qsa_decode call = block scoring, top-k block selection, the
+position buffer and gather attention for the whole batch of one QSA layer.
+Inputs are resident in HBM before timing starts.  To measure HBM rather than
+the 256 MB last-level cache, R identical copies of every input are rotated so
+that successive calls touch at least 1 GiB of distinct bytes.  The K timed
+calls are captured in one HIP graph and bracketed by HIP events.
+
+Prints one JSON line (see the keys below); human-readable detail goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "qsa_decode steps/sec at 50K ctx (B=1,32) + achieved HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+K_TOP = 512
+WIDTH = 4 * K_TOP + 3
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ byte counts
+def query_geometry(w):
+    """(request, L, nf, n_pos) for every query."""
+    out = []
+    for r in range(w.num_req):
+        nq = int(w.q_start[r + 1] - w.q_start[r])
+        for j in range(nq):
+            L = int(w.seq_len[r]) - nq + 1 + j
+            nf = L // 4
+            out.append((r, L, nf, 4 * min(nf, K_TOP) + L % 4))
+    return out
+
+
+def algorithmic_bytes(w) -> dict:
+    """Compulsory HBM bytes per call: every compressed key once per request, the
+    gathered K and V rows, index query, attention query and FP32 output.  The
+    FP32 score buffer and position buffer round trips are listed per kernel."""
+    e = 2 if w.kv_dtype == "bf16" else 1
+    hq, hkv = w.num_q_heads, w.num_kv_heads
+    geo = query_geometry(w)
+    keys = 256 * int(sum(int(s) // 4 for s in w.seq_len))
+    kv = sum(n * hkv * 128 * 2 * e for (_, _, _, n) in geo)
+    step = keys + kv + w.num_q * (256 + hq * 256 + hq * 512)
+    nblk_q = sum(int(w.seq_len[r]) // 4 for (r, _, _, _) in geo)
+    score = keys + 256 * w.num_q + 4 * nblk_q
+    select = sum(4 * nf for (_, _, nf, _) in geo if nf > K_TOP) + w.num_q * 4 * (K_TOP + WIDTH)
+    attn = kv + w.num_q * (hq * 256 + hq * 512) + sum(4 * n for (_, _, _, n) in geo)
+    return {"step": step, "score": score, "select": select, "attn": attn}
+
+
+# ------------------------------------------------------------------ GPU timing
+class Rig:
+    """R rotating device copies of one workload plus the library handles."""
+
+    def __init__(self, w, copies: int):
+        import torch
+        import block_sparse_attention_qsa_amd as qsa
+        from workloads.device import upload
+        self.torch, self.qsa, self.w = torch, qsa, w
+        base = upload(w)
+        self.copies = [base]
+        for _ in range(copies - 1):
+            self.copies.append({k: (v.clone() if v is not None else None) for k, v in base.items()})
+        self.batch = qsa.Batch(w.q_start, w.seq_len, w.kv_start, w.blk_start)
+        hq = w.num_q_heads
+        self.outs = [torch.empty((w.num_q, hq, 128), dtype=torch.float32, device="cuda") for _ in self.copies]
+        self.ws = qsa.alloc_workspace(self.batch, hq, w.num_kv_heads)
+        self.sm = 1.0 / math.sqrt(128)
+        # stage inputs for the per-kernel timings
+        self.scores = torch.zeros((w.num_q, max(self.batch.max_blocks, 1)), dtype=torch.float32, device="cuda")
+        self.sel = torch.empty((w.num_q, K_TOP), dtype=torch.int32, device="cuda")
+        self.n_sel = torch.empty((w.num_q,), dtype=torch.int32, device="cuda")
+        self.pos = torch.empty((w.num_q, WIDTH), dtype=torch.int32, device="cuda")
+        self.n_pos = torch.empty((w.num_q,), dtype=torch.int32, device="cuda")
+        self.attn_ws = qsa.alloc_workspace(self.batch, hq, w.num_kv_heads)
+
+    def decode(self, i):
+        c = self.copies[i % len(self.copies)]
+        self.qsa.qsa_decode(self.batch, c["idx_q"], c["ckeys"], c["q"], c["k_cache"], c["v_cache"],
+                            self.outs[i % len(self.copies)], self.ws, k_scale=c["k_scale"],
+                            v_scale=c["v_scale"], sm_scale=self.sm)
+
+    def prepare_stage_inputs(self):
+        c = self.copies[0]
+        self.qsa.qsa_score(self.batch, c["idx_q"], c["ckeys"], self.scores)
+        self.qsa.qsa_select_topk(self.batch, self.scores, self.sel, self.n_sel)
+        self.qsa.qsa_build_index(self.batch, self.sel, self.n_sel, self.pos, self.n_pos)
+        self.torch.cuda.synchronize()
+
+    def stage(self, name, i):
+        c = self.copies[i % len(self.copies)]
+        if name == "score":
+            self.qsa.qsa_score(self.batch, c["idx_q"], c["ckeys"], self.scores)
+        elif name == "select":
+            self.qsa.qsa_select_topk(self.batch, self.scores, self.sel, self.n_sel)
+        elif name == "attn":
+            self.qsa.qsa_sparse_attn(self.batch, c["q"], c["k_cache"], c["v_cache"], self.pos, self.n_pos,
+                                     self.outs[i % len(self.copies)], k_scale=c["k_scale"], v_scale=c["v_scale"],
+                                     sm_scale=self.sm, workspace=self.attn_ws)
+        else:
+            raise KeyError(name)
+
+    def timed_graph(self, fn, steps: int, warmup: int, reps: int = 3):
+        """Capture `steps` calls of fn(i) in a HIP graph; return (median ms per
+        call over reps replays, wall-clock ms per call of the last replay)."""
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                fn(i)
+        torch.cuda.synchronize()
+        g.replay()                      # untimed first replay
+        torch.cuda.synchronize()
+        times = []
+        wall = None
+        for _ in range(reps):
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            start.record()
+            g.replay()
+            end.record()
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) * 1e3 / steps
+            times.append(start.elapsed_time(end) / steps)
+        del g
+        return float(np.median(times)), wall
+
+
+def rotation_copies(w, touched: int, limit_bytes: float = 80e9) -> int:
+    per_copy = (w.k_cache.nbytes + w.v_cache.nbytes + w.ckeys.nbytes + w.q.nbytes + w.idx_q.nbytes)
+    want = max(1, math.ceil((1 << 30) / max(touched, 1)))
+    return int(max(1, min(want, limit_bytes // max(per_copy, 1))))
+
+
+def measure(name: str, steps: int, warmup: int, kernels: bool = True) -> dict:
+    from workloads import make_workload
+    t0 = time.perf_counter()
+    w = make_workload(name)
+    log(f"[{name}] generated in {time.perf_counter() - t0:.1f}s: {w.num_req} requests, {w.num_q} queries")
+    nbytes = algorithmic_bytes(w)
+    R = rotation_copies(w, nbytes["step"])
+    rig = Rig(w, R)
+    log(f"[{name}] {R} rotating copies, {nbytes['step'] / 1e6:.2f} MB algorithmic per step")
+    ms, wall_ms = rig.timed_graph(rig.decode, steps, warmup)
+    gbps = nbytes["step"] / (ms * 1e-3) / 1e9
+    log(f"[{name}] qsa_decode: {ms * 1e3:.2f} us/step (graph, events), wall {wall_ms * 1e3:.2f} us/step, "
+        f"{gbps:.0f} GB/s = {gbps / HBM_PEAK_GBPS:.1%} of HBM peak")
+    res = {"workload": name, "w": w, "copies": R, "ms_per_step": ms, "wall_ms_per_step": wall_ms,
+           "steps_per_s": 1e3 / ms, "step_bytes": nbytes["step"], "step_gbps": gbps, "kernels": {}}
+    if kernels:
+        rig.prepare_stage_inputs()
+        for st in ("score", "select", "attn"):
+            kms, _ = rig.timed_graph(lambda i, st=st: rig.stage(st, i), steps, warmup)
+            kg = nbytes[st] / (kms * 1e-3) / 1e9
+            res["kernels"][st] = {"us": kms * 1e3, "bytes": nbytes[st], "gbps": kg}
+            log(f"[{name}]   {st:6s}: {kms * 1e3:8.2f} us/launch, {nbytes[st] / 1e6:8.3f} MB, {kg:7.0f} GB/s")
+    del rig
+    import torch
+    torch.cuda.empty_cache()
+    return res
+
+
+KERNEL_NAMES = {"score": "qsa::score_kernel", "select": "qsa::select_kernel", "attn": "qsa::attn_kernel"}
+
+
+def roofline_of(res: dict, traffic: dict | None) -> dict:
+    ks = res["kernels"]
+    dom = max(ks, key=lambda s: ks[s]["us"])
+    k = ks[dom]
+    tr = None
+    if traffic and traffic.get("kernel") == KERNEL_NAMES[dom] and traffic.get("workload") == res["workload"]:
+        tr = traffic.get("bytes_per_launch")
+    return {"kernel": KERNEL_NAMES[dom], "bound": "hbm", "achieved": round(k["gbps"], 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(k["gbps"] / HBM_PEAK_GBPS, 4), "traffic": tr,
+            "algorithmic_bytes_per_launch": k["bytes"], "avg_launch_us": round(k["us"], 3)}
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(name: str, seconds: float) -> dict:
+    import oracle
+    from threadpoolctl import threadpool_limits
+    from workloads import make_workload
+    w = make_workload(name)
+    args = (w.q_start, w.seq_len, w.kv_start, w.blk_start, w.idx_q, w.ckeys, w.q, w.k_cache, w.v_cache,
+            w.kv_dtype, w.k_scale, w.v_scale)
+    n = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            oracle.decode(*args, sm_scale=1.0 / math.sqrt(128), want_scores=False)
+            n += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    log(f"[cpu] oracle: {n} full {name} steps in {dt:.1f}s on 1 thread")
+    return {"value": round(n / dt, 4), "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} full {name} steps ({w.num_q} queries each), single thread, "
+                      f"{os.cpu_count()} host CPUs visible"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default="mtp50k")
+    ap.add_argument("--b32", default="mtp50k_b32_fp8", help="second workload reported beside (or 'none')")
+    ap.add_argument("--b32-steps", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timings")
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="HBM traffic per launch measured by rocprofv3 counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import block_sparse_attention_qsa_amd as qsa
+    qsa.lib()
+
+    res = measure(args.config, args.steps, args.warmup, kernels=not args.no_kernels)
+    w = res.pop("w")
+    traffic = None
+    if os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f)
+    line = {
+        "metric": METRIC, "value": round(res["steps_per_s"], 2), "unit": "steps/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.kv_dtype == "bf16" else "bf16+fp8kv", "data": "synthetic",
+        "config": {"workload": args.config, "requests": w.num_req, "queries": w.num_q,
+                   "seq_len": int(w.seq_len.max()), "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "kv_dtype": w.kv_dtype, "topk": K_TOP, "rotation_copies": res["copies"]},
+        "step_gbps": round(res["step_gbps"], 1), "step_frac_of_peak": round(res["step_gbps"] / HBM_PEAK_GBPS, 4),
+        "wall_ms_per_step": round(res["wall_ms_per_step"], 6),
+        "kernels_us": {k: round(v["us"], 3) for k, v in res["kernels"].items()},
+    }
+    if res["kernels"]:
+        line["roofline"] = roofline_of(res, traffic)
+    if args.b32 != "none":
+        r2 = measure(args.b32, args.b32_steps, min(args.warmup, 20), kernels=not args.no_kernels)
+        w2 = r2.pop("w")
+        line["b32"] = {"workload": args.b32, "steps_per_s": round(r2["steps_per_s"], 2),
+                       "ms_per_step": round(r2["ms_per_step"], 6), "step_gbps": round(r2["step_gbps"], 1),
+                       "step_frac_of_peak": round(r2["step_gbps"] / HBM_PEAK_GBPS, 4),
+                       "kernels_us": {k: round(v["us"], 3) for k, v in r2["kernels"].items()},
+                       "requests": w2.num_req, "queries": w2.num_q, "kv_dtype": w2.kv_dtype,
+                       "rotation_copies": r2["copies"]}
+        if r2["kernels"]:
+            line["b32"]["roofline"] = roofline_of(r2, traffic)
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

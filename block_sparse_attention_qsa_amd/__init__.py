@@ -1,0 +1,271 @@
+"""QSA block-sparse decode attention on MI355X (gfx950).
+
+Thin Python binding of libqsa.so (C ABI in include/qsa.h).  Each function
+here marshals torch tensors to device pointers and the current HIP stream and
+calls the entry point of the same name; every step of the computation runs in
+the library's HIP kernels.  PyTorch provides device memory and streams only.
+
+There is no fallback: if the library is not built, or a call fails, a
+QsaError is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["QsaError", "Batch", "lib", "abi_version", "status_string", "workspace_bytes", "alloc_workspace",
+           "qsa_score", "qsa_select_topk", "qsa_build_index", "qsa_sparse_attn", "qsa_decode",
+           "BLOCK", "TOPK", "WIDTH", "INDEX_DIM", "HEAD_DIM", "KV_BF16", "KV_FP8_E4M3", "OUT_F32", "OUT_BF16"]
+
+BLOCK = 4
+TOPK = 512
+WIDTH = BLOCK * TOPK + BLOCK - 1
+INDEX_DIM = 128
+HEAD_DIM = 128
+KV_BF16, KV_FP8_E4M3 = 0, 1
+OUT_F32, OUT_BF16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqsa.so")
+
+
+class QsaError(RuntimeError):
+    pass
+
+
+class _CBatch(ctypes.Structure):
+    _fields_ = [("num_req", ctypes.c_int32), ("num_q", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("q_start", ctypes.c_void_p), ("seq_len", ctypes.c_void_p), ("kv_start", ctypes.c_void_p),
+                ("blk_start", ctypes.c_void_p)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "qsa_abi_version": (ctypes.c_int, []),
+    "qsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "qsa_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32]),
+    "qsa_score": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P]),
+    "qsa_select_topk": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _P, _SZ, _P]),
+    "qsa_build_index": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _P]),
+    "qsa_sparse_attn": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P, _P, _I32, _F, _P, _I32,
+                                       _P, _SZ, _P]),
+    "qsa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _F, _P, _I32,
+                                  _P, _P, _P, _P, _P, _SZ, _P]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqsa.so (built in-tree by block_sparse_attention_qsa_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise QsaError(f"{LIB_PATH} is not built; run `python -m block_sparse_attention_qsa_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def abi_version() -> int:
+    return lib().qsa_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib().qsa_status_string(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise QsaError(f"{what}: {status_string(status)} (status {status})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, shape=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise QsaError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise QsaError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise QsaError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise QsaError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_FP8 = (torch.float8_e4m3fn, torch.uint8)
+
+
+class Batch:
+    """Batch metadata: per-request query ranges, lengths and cache offsets.
+
+    Host arrays (numpy / CPU tensors / lists) are copied to `device` and the
+    host scalars (num_req, num_q, max_blocks) derived from them.  Device int32
+    tensors are used as they are and then num_q and max_blocks must be given.
+    """
+
+    def __init__(self, q_start, seq_len, kv_start, blk_start, *, num_q: Optional[int] = None,
+                 max_blocks: Optional[int] = None, device="cuda"):
+        def to_dev(x):
+            if isinstance(x, torch.Tensor) and x.is_cuda:
+                if x.dtype != torch.int32 or not x.is_contiguous():
+                    raise QsaError("device metadata must be contiguous int32")
+                return x
+            return torch.as_tensor(x, dtype=torch.int32).contiguous().to(device)
+
+        host = not (isinstance(seq_len, torch.Tensor) and seq_len.is_cuda)
+        if host:
+            qs = [int(v) for v in (q_start.tolist() if hasattr(q_start, "tolist") else q_start)]
+            sl = [int(v) for v in (seq_len.tolist() if hasattr(seq_len, "tolist") else seq_len)]
+            num_q = qs[-1] if num_q is None else num_q
+            max_blocks = max(s // BLOCK for s in sl) if max_blocks is None else max_blocks
+        if num_q is None or max_blocks is None:
+            raise QsaError("num_q and max_blocks are required with device metadata")
+        self.q_start = to_dev(q_start)
+        self.seq_len = to_dev(seq_len)
+        self.kv_start = to_dev(kv_start)
+        self.blk_start = to_dev(blk_start)
+        self.num_req = int(self.seq_len.shape[0])
+        self.num_q = int(num_q)
+        self.max_blocks = int(max_blocks)
+        self._c = _CBatch(self.num_req, self.num_q, self.max_blocks, self.q_start.data_ptr(),
+                          self.seq_len.data_ptr(), self.kv_start.data_ptr(), self.blk_start.data_ptr())
+
+    @property
+    def c(self):
+        return ctypes.byref(self._c)
+
+
+def workspace_bytes(batch: Batch, num_q_heads: int, num_kv_heads: int, k: int = TOPK) -> int:
+    return int(lib().qsa_workspace_bytes(batch.c, num_q_heads, num_kv_heads, k))
+
+
+def alloc_workspace(batch: Batch, num_q_heads: int, num_kv_heads: int, k: int = TOPK,
+                    device="cuda") -> torch.Tensor:
+    """A zero-filled workspace of the size the library asks for (the library
+    keeps it zeroed between calls)."""
+    n = workspace_bytes(batch, num_q_heads, num_kv_heads, k)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def qsa_score(batch: Batch, idx_q, ckeys, scores, stream=None) -> None:
+    _dev(idx_q, "idx_q", _BF16, (batch.num_q, INDEX_DIM))
+    _dev(ckeys, "ckeys", _BF16)
+    if ckeys.dim() != 2 or ckeys.shape[1] != INDEX_DIM:
+        raise QsaError("ckeys must be [rows, 128]")
+    _dev(scores, "scores", (torch.float32,))
+    if scores.dim() != 2 or scores.shape[0] != batch.num_q:
+        raise QsaError("scores must be [num_q, ld]")
+    _check(lib().qsa_score(batch.c, _ptr(idx_q), _ptr(ckeys), _ptr(scores), scores.shape[1], _stream(stream)),
+           "qsa_score")
+
+
+def qsa_select_topk(batch: Batch, scores, sel, n_sel, k: int = TOPK, workspace=None, stream=None) -> None:
+    _dev(scores, "scores", (torch.float32,))
+    if scores.dim() != 2 or scores.shape[0] != batch.num_q:
+        raise QsaError("scores must be [num_q, ld]")
+    _dev(sel, "sel", (torch.int32,), (batch.num_q, k))
+    _dev(n_sel, "n_sel", (torch.int32,), (batch.num_q,))
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().qsa_select_topk(batch.c, _ptr(scores), scores.shape[1], k, _ptr(sel), _ptr(n_sel),
+                                 _ptr(workspace), ws_n, _stream(stream)), "qsa_select_topk")
+
+
+def qsa_build_index(batch: Batch, sel, n_sel, pos, n_pos, k: int = TOPK, stream=None) -> None:
+    _dev(sel, "sel", (torch.int32,), (batch.num_q, k))
+    _dev(n_sel, "n_sel", (torch.int32,), (batch.num_q,))
+    _dev(pos, "pos", (torch.int32,), (batch.num_q, BLOCK * k + BLOCK - 1))
+    _dev(n_pos, "n_pos", (torch.int32,), (batch.num_q,))
+    _check(lib().qsa_build_index(batch.c, _ptr(sel), _ptr(n_sel), k, _ptr(pos), _ptr(n_pos), _stream(stream)),
+           "qsa_build_index")
+
+
+def _kv_args(k_cache, v_cache, k_scale, v_scale, num_kv_heads):
+    if k_cache.dtype in _FP8:
+        kv = KV_FP8_E4M3
+        _dev(k_cache, "k_cache", _FP8)
+        _dev(v_cache, "v_cache", _FP8)
+        _dev(k_scale, "k_scale", (torch.float32,), (num_kv_heads,))
+        _dev(v_scale, "v_scale", (torch.float32,), (num_kv_heads,))
+    else:
+        kv = KV_BF16
+        _dev(k_cache, "k_cache", _BF16)
+        _dev(v_cache, "v_cache", _BF16)
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dim() != 3 or t.shape[1] != num_kv_heads or t.shape[2] != HEAD_DIM:
+            raise QsaError(f"{name} must be [slots, {num_kv_heads}, {HEAD_DIM}]")
+    return kv
+
+
+def _out_dtype(out) -> int:
+    if out.dtype == torch.float32:
+        return OUT_F32
+    if out.dtype == torch.bfloat16:
+        return OUT_BF16
+    raise QsaError("out must be float32 or bfloat16")
+
+
+def qsa_sparse_attn(batch: Batch, q, k_cache, v_cache, pos, n_pos, out, *, k_scale=None, v_scale=None,
+                    sm_scale: Optional[float] = None, workspace=None, stream=None) -> None:
+    if q.dim() != 3 or q.shape[0] != batch.num_q or q.shape[2] != HEAD_DIM:
+        raise QsaError("q must be [num_q, Hq, 128]")
+    hq, hkv = int(q.shape[1]), int(k_cache.shape[1])
+    _dev(q, "q", _BF16)
+    kv = _kv_args(k_cache, v_cache, k_scale, v_scale, hkv)
+    _dev(pos, "pos", (torch.int32,))
+    _dev(n_pos, "n_pos", (torch.int32,), (batch.num_q,))
+    _dev(out, "out", (torch.float32, torch.bfloat16), (batch.num_q, hq, HEAD_DIM))
+    sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else float(sm_scale)
+    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().qsa_sparse_attn(batch.c, _ptr(q), _ptr(k_cache), _ptr(v_cache), kv, _ptr(k_scale), _ptr(v_scale),
+                                 hq, hkv, _ptr(pos), _ptr(n_pos), pos.shape[1], sm, _ptr(out), _out_dtype(out),
+                                 _ptr(workspace), ws_n, _stream(stream)), "qsa_sparse_attn")
+
+
+def qsa_decode(batch: Batch, idx_q, ckeys, q, k_cache, v_cache, out, workspace, *, k_scale=None, v_scale=None,
+               k: int = TOPK, sm_scale: Optional[float] = None, sel=None, n_sel=None, pos=None, n_pos=None,
+               stream=None) -> None:
+    _dev(idx_q, "idx_q", _BF16, (batch.num_q, INDEX_DIM))
+    _dev(ckeys, "ckeys", _BF16)
+    if q.dim() != 3 or q.shape[0] != batch.num_q or q.shape[2] != HEAD_DIM:
+        raise QsaError("q must be [num_q, Hq, 128]")
+    hq, hkv = int(q.shape[1]), int(k_cache.shape[1])
+    _dev(q, "q", _BF16)
+    kv = _kv_args(k_cache, v_cache, k_scale, v_scale, hkv)
+    _dev(out, "out", (torch.float32, torch.bfloat16), (batch.num_q, hq, HEAD_DIM))
+    width = BLOCK * k + BLOCK - 1
+    if sel is not None:
+        _dev(sel, "sel", (torch.int32,), (batch.num_q, k))
+    if n_sel is not None:
+        _dev(n_sel, "n_sel", (torch.int32,), (batch.num_q,))
+    if pos is not None:
+        _dev(pos, "pos", (torch.int32,), (batch.num_q, width))
+    if n_pos is not None:
+        _dev(n_pos, "n_pos", (torch.int32,), (batch.num_q,))
+    _dev(workspace, "workspace", (torch.uint8,))
+    sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else float(sm_scale)
+    _check(lib().qsa_decode(batch.c, _ptr(idx_q), _ptr(ckeys), _ptr(q), _ptr(k_cache), _ptr(v_cache), kv,
+                            _ptr(k_scale), _ptr(v_scale), hq, hkv, k, sm, _ptr(out), _out_dtype(out),
+                            _ptr(sel), _ptr(n_sel), _ptr(pos), _ptr(n_pos), _ptr(workspace),
+                            workspace.numel(), _stream(stream)), "qsa_decode")

@@ -1,0 +1,223 @@
+// C ABI of libqsa.so: host-side validation, workspace layout and dispatch of
+// the QSA kernels.  Every entry point only enqueues work on the caller's
+// stream; see include/qsa.h for the contract of each call.
+#include <math.h>
+
+#include "qsa.h"
+#include "qsa_common.hpp"
+#include "qsa_launch.hpp"
+
+namespace {
+
+using qsa::Meta;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct WsLayout {
+  size_t counters, partials, attn_end, scores, sel, n_sel, pos, n_pos, total;
+};
+
+WsLayout ws_layout(int num_q, int max_blocks, int hq, int hkv, int k) {
+  WsLayout w;
+  const int width = QSA_BLOCK * k + QSA_BLOCK - 1;
+  size_t off = 0;
+  w.counters = off; off += align_up((size_t)num_q * hkv * sizeof(uint32_t));
+  w.partials = off; off += align_up(qsa::attn_partial_bytes(num_q, hkv, hq / hkv, width));
+  w.attn_end = off;
+  w.scores = off; off += align_up((size_t)num_q * (size_t)(max_blocks > 0 ? max_blocks : 1) * sizeof(float));
+  w.sel = off; off += align_up((size_t)num_q * k * sizeof(int32_t));
+  w.n_sel = off; off += align_up((size_t)num_q * sizeof(int32_t));
+  w.pos = off; off += align_up((size_t)num_q * width * sizeof(int32_t));
+  w.n_pos = off; off += align_up((size_t)num_q * sizeof(int32_t));
+  w.total = off;
+  return w;
+}
+
+qsa_status check_batch(const qsa_batch* b) {
+  if (!b) return QSA_ERR_NULL;
+  if (!b->q_start || !b->seq_len || !b->kv_start || !b->blk_start) return QSA_ERR_NULL;
+  if (b->num_req < 1 || b->num_req > QSA_MAX_REQUESTS) return QSA_ERR_SHAPE;
+  if (b->num_q < b->num_req || b->num_q > QSA_MAX_Q_PER_REQ * b->num_req) return QSA_ERR_SHAPE;
+  if (b->max_blocks < 0 || b->max_blocks > (1 << 28)) return QSA_ERR_SHAPE;
+  return QSA_OK;
+}
+
+qsa_status check_heads(int32_t hq, int32_t hkv) {
+  if (hq < 1 || hkv < 1 || hq % hkv != 0) return QSA_ERR_SHAPE;
+  if (hq / hkv > QSA_MAX_GQA_GROUP) return QSA_ERR_UNSUPPORTED;
+  if ((int64_t)hq * hkv > (1 << 16)) return QSA_ERR_SHAPE;
+  return QSA_OK;
+}
+
+qsa_status check_k(int32_t k) { return (k < 1 || k > QSA_TOPK) ? QSA_ERR_SHAPE : QSA_OK; }
+
+qsa_status check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return QSA_OK;
+  if (!ws || ws_bytes < need || ((uintptr_t)ws % kAlign) != 0) return QSA_ERR_WORKSPACE;
+  return QSA_OK;
+}
+
+qsa_status check_attn_args(const void* q, const void* kc, const void* vc, int32_t kv_dtype, const float* ks,
+                           const float* vs, float sm_scale, void* out, int32_t out_dtype) {
+  if (!q || !kc || !vc || !out) return QSA_ERR_NULL;
+  if (kv_dtype != QSA_KV_BF16 && kv_dtype != QSA_KV_FP8_E4M3) return QSA_ERR_UNSUPPORTED;
+  if (kv_dtype == QSA_KV_FP8_E4M3 && (!ks || !vs)) return QSA_ERR_NULL;
+  if (out_dtype != QSA_OUT_F32 && out_dtype != QSA_OUT_BF16) return QSA_ERR_UNSUPPORTED;
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return QSA_ERR_SHAPE;
+  return QSA_OK;
+}
+
+Meta meta_of(const qsa_batch* b) {
+  Meta m;
+  m.num_req = b->num_req;
+  m.num_q = b->num_q;
+  m.max_blocks = b->max_blocks;
+  m.q_start = b->q_start;
+  m.seq_len = b->seq_len;
+  m.kv_start = b->kv_start;
+  m.blk_start = b->blk_start;
+  return m;
+}
+
+inline qsa_status launched(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA_ERR_LAUNCH; }
+
+#define QSA_TRY(x)                  \
+  do {                              \
+    qsa_status st_ = (x);           \
+    if (st_ != QSA_OK) return st_;  \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int qsa_abi_version(void) { return QSA_ABI_VERSION; }
+
+const char* qsa_status_string(int status) {
+  switch (status) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_NULL: return "a required pointer is NULL";
+    case QSA_ERR_SHAPE: return "a size argument is out of range or inconsistent";
+    case QSA_ERR_UNSUPPORTED: return "unsupported dtype or head geometry";
+    case QSA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case QSA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t qsa_workspace_bytes(const qsa_batch* batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t k) {
+  if (check_batch(batch) != QSA_OK || check_heads(num_q_heads, num_kv_heads) != QSA_OK || check_k(k) != QSA_OK)
+    return 0;
+  return ws_layout(batch->num_q, batch->max_blocks, num_q_heads, num_kv_heads, k).total;
+}
+
+qsa_status qsa_score(const qsa_batch* batch, const void* idx_q, const void* ckeys, float* scores, int64_t ld,
+                     hipStream_t stream) {
+  QSA_TRY(check_batch(batch));
+  if (!idx_q || !ckeys || !scores) return QSA_ERR_NULL;
+  if (ld < batch->max_blocks) return QSA_ERR_SHAPE;
+  return launched(qsa::launch_score(meta_of(batch), idx_q, ckeys, scores, ld, stream));
+}
+
+qsa_status qsa_select_topk(const qsa_batch* batch, const float* scores, int64_t ld, int32_t k, int32_t* sel,
+                           int32_t* n_sel, void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  QSA_TRY(check_batch(batch));
+  QSA_TRY(check_k(k));
+  if (!scores || !sel || !n_sel) return QSA_ERR_NULL;
+  if (ld < batch->max_blocks) return QSA_ERR_SHAPE;
+  return launched(qsa::launch_select(meta_of(batch), scores, ld, k, sel, n_sel, nullptr, nullptr,
+                                     QSA_BLOCK * k + QSA_BLOCK - 1, stream));
+}
+
+qsa_status qsa_build_index(const qsa_batch* batch, const int32_t* sel, const int32_t* n_sel, int32_t k,
+                           int32_t* pos, int32_t* n_pos, hipStream_t stream) {
+  QSA_TRY(check_batch(batch));
+  QSA_TRY(check_k(k));
+  if (!sel || !n_sel || !pos || !n_pos) return QSA_ERR_NULL;
+  return launched(qsa::launch_build_index(meta_of(batch), sel, n_sel, k, pos, n_pos,
+                                          QSA_BLOCK * k + QSA_BLOCK - 1, stream));
+}
+
+qsa_status qsa_sparse_attn(const qsa_batch* batch, const void* q, const void* k_cache, const void* v_cache,
+                           int32_t kv_dtype, const float* k_scale, const float* v_scale, int32_t num_q_heads,
+                           int32_t num_kv_heads, const int32_t* pos, const int32_t* n_pos, int32_t width,
+                           float sm_scale, void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  QSA_TRY(check_batch(batch));
+  QSA_TRY(check_heads(num_q_heads, num_kv_heads));
+  QSA_TRY(check_attn_args(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, sm_scale, out, out_dtype));
+  if (!pos || !n_pos) return QSA_ERR_NULL;
+  if (width < QSA_BLOCK + QSA_BLOCK - 1 || width > QSA_WIDTH || (width - (QSA_BLOCK - 1)) % QSA_BLOCK != 0)
+    return QSA_ERR_SHAPE;
+  const int k = (width - (QSA_BLOCK - 1)) / QSA_BLOCK;
+  const WsLayout w = ws_layout(batch->num_q, batch->max_blocks, num_q_heads, num_kv_heads, k);
+  QSA_TRY(check_ws(ws, ws_bytes, w.attn_end));
+  char* base = static_cast<char*>(ws);
+  qsa::AttnArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.kv_fp8 = kv_dtype == QSA_KV_FP8_E4M3;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.pos = pos;
+  a.n_pos = n_pos;
+  a.width = width;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.out_bf16 = out_dtype == QSA_OUT_BF16;
+  a.partials = reinterpret_cast<float*>(base + w.partials);
+  a.counters = reinterpret_cast<uint32_t*>(base + w.counters);
+  return launched(qsa::launch_attn(meta_of(batch), a, stream));
+}
+
+qsa_status qsa_decode(const qsa_batch* batch, const void* idx_q, const void* ckeys, const void* q,
+                      const void* k_cache, const void* v_cache, int32_t kv_dtype, const float* k_scale,
+                      const float* v_scale, int32_t num_q_heads, int32_t num_kv_heads, int32_t k, float sm_scale,
+                      void* out, int32_t out_dtype, int32_t* sel_opt, int32_t* n_sel_opt, int32_t* pos_opt,
+                      int32_t* n_pos_opt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  QSA_TRY(check_batch(batch));
+  QSA_TRY(check_heads(num_q_heads, num_kv_heads));
+  QSA_TRY(check_k(k));
+  QSA_TRY(check_attn_args(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, sm_scale, out, out_dtype));
+  if (!idx_q || !ckeys) return QSA_ERR_NULL;
+  const WsLayout w = ws_layout(batch->num_q, batch->max_blocks, num_q_heads, num_kv_heads, k);
+  QSA_TRY(check_ws(ws, ws_bytes, w.total));
+  const int width = QSA_BLOCK * k + QSA_BLOCK - 1;
+  char* base = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(base + w.scores);
+  int32_t* sel = sel_opt ? sel_opt : reinterpret_cast<int32_t*>(base + w.sel);
+  int32_t* n_sel = n_sel_opt ? n_sel_opt : reinterpret_cast<int32_t*>(base + w.n_sel);
+  int32_t* pos = pos_opt ? pos_opt : reinterpret_cast<int32_t*>(base + w.pos);
+  int32_t* n_pos = n_pos_opt ? n_pos_opt : reinterpret_cast<int32_t*>(base + w.n_pos);
+  const Meta m = meta_of(batch);
+  const int64_t ld = batch->max_blocks > 0 ? batch->max_blocks : 1;
+
+  QSA_TRY(launched(qsa::launch_score(m, idx_q, ckeys, scores, ld, stream)));
+  QSA_TRY(launched(qsa::launch_select(m, scores, ld, k, sel, n_sel, pos, n_pos, width, stream)));
+  qsa::AttnArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.kv_fp8 = kv_dtype == QSA_KV_FP8_E4M3;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.pos = pos;
+  a.n_pos = n_pos;
+  a.width = width;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.out_bf16 = out_dtype == QSA_OUT_BF16;
+  a.partials = reinterpret_cast<float*>(base + w.partials);
+  a.counters = reinterpret_cast<uint32_t*>(base + w.counters);
+  return launched(qsa::launch_attn(m, a, stream));
+}
+
+}  // extern "C"

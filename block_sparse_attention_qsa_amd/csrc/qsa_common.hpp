@@ -1,0 +1,112 @@
+// Device-side helpers shared by the QSA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qsa.h"
+
+namespace qsa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kChunk = 32;             // positions per attention step of one wave
+constexpr int kAttnWaves = 4;          // waves per attention workgroup
+constexpr int kSelectThreads = 1024;   // threads of one top-k workgroup
+constexpr int kRadixBins = 2048;       // 11-bit digits: passes over bits 31..21, 20..10, 9..0
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Index of the request that owns query q: the largest r with q_start[r] <= q.
+__device__ __forceinline__ int request_of(const int32_t* __restrict__ q_start, int num_req, int q) {
+  int lo = 0, hi = num_req - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (q_start[mid] <= q) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Order-preserving map FP32 -> uint32 (larger float -> larger key); -0.0 maps
+// like +0.0 so that the two compare equal.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// DPP sum over the 16 lanes of a row; every lane of the row gets the total.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+__device__ __forceinline__ float fdot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                         c, false);
+}
+
+// Wave-wide inclusive prefix sum of unsigned values.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    uint32_t t = __shfl_up(v, off, kWave);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+// Block-wide exclusive prefix sum for blockDim.x == NT (multiple of 64).
+// `scratch` needs NT/64 + 1 words of LDS.  Returns the exclusive prefix of
+// this thread and writes the block total to *total.  Contains two barriers.
+template <int NT>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
+  constexpr int NW = NT / kWave;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  uint32_t inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) scratch[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t w = lane < NW ? scratch[lane] : 0u;
+    uint32_t wi = wave_inclusive_scan(w);
+    if (lane < NW) scratch[lane] = wi - w;
+    if (lane == NW - 1) scratch[NW] = wi;
+  }
+  __syncthreads();
+  *total = scratch[NW];
+  return scratch[wave] + inc - v;
+}
+
+// Attention split geometry shared by the launcher and the workspace sizing.
+struct AttnSplit {
+  int splits;            // workgroups per (query, KV head)
+  int chunks_per_split;  // 32-position chunks per workgroup (multiple of kAttnWaves)
+};
+
+__host__ __device__ inline AttnSplit attn_split(int num_q, int num_kv_heads, int width) {
+  const int chunks = (width + kChunk - 1) / kChunk;
+  const int units = num_q * num_kv_heads;
+  const int target_wgs = 1024;
+  int splits = (target_wgs + units - 1) / units;
+  int max_splits = (chunks + kAttnWaves - 1) / kAttnWaves;
+  if (splits > max_splits) splits = max_splits;
+  if (splits < 1) splits = 1;
+  int cps = (chunks + splits - 1) / splits;
+  cps = (cps + kAttnWaves - 1) / kAttnWaves * kAttnWaves;
+  splits = (chunks + cps - 1) / cps;
+  AttnSplit a;
+  a.splits = splits;
+  a.chunks_per_split = cps;
+  return a;
+}
+
+}  // namespace qsa

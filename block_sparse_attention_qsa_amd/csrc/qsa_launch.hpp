@@ -1,0 +1,47 @@
+// Host-side launchers of the QSA kernels (internal to libqsa.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qsa {
+
+struct Meta {
+  int num_req, num_q, max_blocks;
+  const int32_t* q_start;
+  const int32_t* seq_len;
+  const int32_t* kv_start;
+  const int32_t* blk_start;
+};
+
+struct AttnArgs {
+  const void* q;            // BF16 [num_q][Hq][128]
+  const void* k_cache;      // [slots][Hkv][128] BF16 or FP8
+  const void* v_cache;
+  const float* k_scale;     // [Hkv] (FP8 only)
+  const float* v_scale;
+  int kv_fp8;
+  int num_q_heads, num_kv_heads;
+  const int32_t* pos;       // [num_q][width]
+  const int32_t* n_pos;     // [num_q]
+  int width;
+  float sm_scale;
+  void* out;                // [num_q][Hq][128]
+  int out_bf16;
+  float* partials;          // split partial results (workspace)
+  uint32_t* counters;       // [num_q][Hkv] split arrival counters (workspace, zero)
+};
+
+hipError_t launch_score(const Meta& m, const void* idx_q, const void* ckeys, float* scores, int64_t ld,
+                        hipStream_t stream);
+// Writes sel/n_sel, and pos/n_pos too when pos != nullptr.
+hipError_t launch_select(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel,
+                         int32_t* n_sel, int32_t* pos, int32_t* n_pos, int width, hipStream_t stream);
+hipError_t launch_build_index(const Meta& m, const int32_t* sel, const int32_t* n_sel, int k, int32_t* pos,
+                              int32_t* n_pos, int width, hipStream_t stream);
+hipError_t launch_attn(const Meta& m, const AttnArgs& a, hipStream_t stream);
+
+// Bytes of split partials the attention needs for this geometry.
+size_t attn_partial_bytes(int num_q, int num_kv_heads, int group, int width);
+
+}  // namespace qsa

@@ -1,0 +1,156 @@
+/*
+ * qsa.h - C ABI of the QSA block-sparse decode attention library (libqsa.so).
+ *
+ * The operation follows the QSA selection pipeline described in the
+ * arex-research.com article on TokenSpeed serving Qwen3.8-Flash-Next, section
+ * on the four optimisations (sparse selection, CuTe DSL kernels, MTP reuse),
+ * items 1-3, and the 10100.com article's section on the first optimisation:
+ *
+ *   tokens are grouped into 4-token micro-blocks, each full block has a
+ *   compressed index key; every query scores all of its full blocks into an
+ *   FP32 buffer (a1), keeps at most 512 of them by top-k (a2), keeps its current
+ *   partial block without selection, which fixes the position buffer at 2,051
+ *   entries (a3), and attends only over those positions with BF16 queries and
+ *   BF16 or FP8 E4M3 KV (a4).  Up to 4 MTP-verify queries of one request share
+ *   every compressed-key load.
+ *
+ * Conventions for every entry point
+ *   - Pointers marked [dev] are device memory owned by the caller; [host] are
+ *     host memory read during the call only.  The library allocates, frees and
+ *     synchronises nothing and never reads device memory back to the host: a
+ *     call validates its host arguments and enqueues kernels on `stream`.
+ *   - Errors are returned as qsa_status; nothing is enqueued when a host-side
+ *     check fails.  QSA_ERR_LAUNCH reports a failed kernel launch.
+ *   - Device-side metadata (the qsa_batch arrays) is trusted: 1 <= nq_r <= 4,
+ *     nq_r <= seq_len[r], request regions inside the caches, scores finite.
+ *     Kernels clamp block counts to max_blocks so that reads of the score
+ *     buffer stay inside [0, ld).
+ *   - Calls on different streams with disjoint outputs and workspaces are
+ *     independent; the library keeps no state between calls.
+ *
+ * Query geometry.  Request r owns queries q_start[r] .. q_start[r+1]-1 (its
+ * nq_r MTP verify queries, or one decode query).  seq_len[r] counts the
+ * request's cached tokens including this step's verify tokens, so verify query
+ * j (0-based) has causal length L = seq_len[r] - nq_r + 1 + j, nf = L / 4 full
+ * blocks and a partial block of L % 4 tokens (nothing when L % 4 == 0).
+ * Token t of request r lives in KV slot kv_start[r] + t; the compressed key of
+ * its full block b is row blk_start[r] + b of the key array.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_ABI_VERSION 1
+#define QSA_BLOCK 4                                  /* tokens per micro-block            */
+#define QSA_TOPK 512                                 /* max full blocks kept per query    */
+#define QSA_WIDTH (QSA_BLOCK * QSA_TOPK + QSA_BLOCK - 1) /* 2,051 position-buffer entries */
+#define QSA_INDEX_DIM 128                            /* compressed key / index query dim  */
+#define QSA_HEAD_DIM 128                             /* attention head dim                */
+#define QSA_MAX_Q_PER_REQ 4                          /* verify queries sharing a key load */
+#define QSA_MAX_GQA_GROUP 16                         /* query heads per KV head           */
+#define QSA_MAX_REQUESTS 65536
+
+typedef enum {
+  QSA_OK = 0,
+  QSA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  QSA_ERR_SHAPE = 2,       /* a size argument is out of range or inconsistent     */
+  QSA_ERR_UNSUPPORTED = 3, /* dtype / head geometry this build does not provide   */
+  QSA_ERR_WORKSPACE = 4,   /* workspace missing, misaligned or too small          */
+  QSA_ERR_LAUNCH = 5       /* the HIP runtime rejected a kernel launch            */
+} qsa_status;
+
+typedef enum { QSA_KV_BF16 = 0, QSA_KV_FP8_E4M3 = 1 } qsa_kv_dtype; /* FP8 = OCP E4M3FN */
+typedef enum { QSA_OUT_F32 = 0, QSA_OUT_BF16 = 1 } qsa_out_dtype;
+
+/* Batch description: host scalars plus device metadata arrays. */
+typedef struct {
+  int32_t num_req;           /* [host] B >= 1                                          */
+  int32_t num_q;             /* [host] total queries = q_start[B]                      */
+  int32_t max_blocks;        /* [host] >= max over r of seq_len[r] / 4                 */
+  const int32_t* q_start;    /* [dev]  int32[B+1], q_start[0] = 0, 1..4 queries each  */
+  const int32_t* seq_len;    /* [dev]  int32[B], cached tokens incl. verify tokens     */
+  const int32_t* kv_start;   /* [dev]  int32[B], first KV slot of request r            */
+  const int32_t* blk_start;  /* [dev]  int32[B], first compressed-key row of request r */
+} qsa_batch;
+
+/* Version of this ABI (QSA_ABI_VERSION). */
+int qsa_abi_version(void);
+
+/* Static, human-readable text for a status code. */
+const char* qsa_status_string(int status);
+
+/* Bytes of device workspace qsa_select_topk / qsa_sparse_attn / qsa_decode need
+ * for this batch and head geometry (0 when none).  The workspace must be
+ * 256-byte aligned and ZERO-FILLED before its first use; every call leaves the
+ * counters it uses at zero again, so one zero fill serves any number of calls
+ * on the same stream.  Calls that overlap in time must not share a workspace. */
+size_t qsa_workspace_bytes(const qsa_batch* batch, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t k);
+
+/* a1 - block scores.  For every query q of request r and every full block
+ * b < seq_len[r] / 4:   scores[q * ld + b] = fp32( sum_d idx_q[q][d] * ckeys[blk_start[r] + b][d] ).
+ * idx_q  [dev] BF16 [num_q][128] row-major; ckeys [dev] BF16 [rows][128] row-major;
+ * scores [dev] FP32 [num_q][ld], ld >= max_blocks.  Products are exact and the sum is
+ * accumulated in FP32 (exact whenever all partial sums are integers below 2^24).
+ * Each key row is read from memory once per request and used for all of its
+ * queries.  Entries b >= seq_len[r] / 4 are not written. */
+qsa_status qsa_score(const qsa_batch* batch, const void* idx_q, const void* ckeys, float* scores,
+                     int64_t ld, hipStream_t stream);
+
+/* a2 - top-k block selection.  For query q with nf full blocks: if nf <= k all
+ * blocks 0..nf-1 are kept; otherwise the k blocks ranked first by (score
+ * descending, block index ascending) are kept - the lower index wins ties and
+ * -0.0 equals +0.0.  sel [dev] int32 [num_q][k] receives the kept block indices in
+ * ascending order, -1 after the last; n_sel [dev] int32 [num_q] their count.
+ * scores as written by qsa_score; 1 <= k <= 512.  ws: qsa_workspace_bytes(). */
+qsa_status qsa_select_topk(const qsa_batch* batch, const float* scores, int64_t ld, int32_t k,
+                           int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* a3 - position buffer.  For query q of request r with n = n_sel[q] kept blocks:
+ *   pos[q][4i + t] = kv_start[r] + 4 * sel[q][i] + t      (i < n, t < 4)
+ *   pos[q][4n + t] = kv_start[r] + 4 * nf + t             (t < L % 4, the partial block)
+ *   pos[q][i]      = -1                                   (i >= n_pos[q], up to 4k+3)
+ * n_pos[q] = 4n + L % 4.  pos [dev] int32 [num_q][4k+3]; n_pos [dev] int32 [num_q]. */
+qsa_status qsa_build_index(const qsa_batch* batch, const int32_t* sel, const int32_t* n_sel,
+                           int32_t k, int32_t* pos, int32_t* n_pos, hipStream_t stream);
+
+/* a4 - gather attention over the position buffer.  For query q and head h with
+ * KV head g = h / (num_q_heads / num_kv_heads):
+ *   out[q][h] = sum_i softmax_i( sm_scale * q[q][h] . K(pos_i, g) ) * V(pos_i, g),  i < n_pos[q]
+ * where K(s, g) is k_cache[s][g][:] (BF16) or its FP8 E4M3FN byte decoded times
+ * k_scale[g] (likewise V with v_scale).  q [dev] BF16 [num_q][Hq][128];
+ * k_cache, v_cache [dev] [slots][Hkv][128] of BF16 or FP8; k_scale, v_scale [dev]
+ * FP32 [Hkv], required for FP8 and ignored for BF16; pos, n_pos as from
+ * qsa_build_index with width = 4k+3; out [dev] [num_q][Hq][128] FP32 or BF16.
+ * Hq % Hkv == 0 and Hq / Hkv <= 16.  ws: qsa_workspace_bytes() for this k. */
+qsa_status qsa_sparse_attn(const qsa_batch* batch, const void* q, const void* k_cache,
+                           const void* v_cache, int32_t kv_dtype, const float* k_scale,
+                           const float* v_scale, int32_t num_q_heads, int32_t num_kv_heads,
+                           const int32_t* pos, const int32_t* n_pos, int32_t width,
+                           float sm_scale, void* out, int32_t out_dtype, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* a1..a4 in one call, the whole decode / MTP-verify step of one QSA layer for
+ * the batch: scores, selection and positions live in the workspace, and
+ * sel_opt [num_q][k] / n_sel_opt / pos_opt [num_q][4k+3] / n_pos_opt, when not
+ * NULL, receive copies of the selection and position buffers for inspection.
+ * Arguments as for the stage calls above. */
+qsa_status qsa_decode(const qsa_batch* batch, const void* idx_q, const void* ckeys, const void* q,
+                      const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                      const float* k_scale, const float* v_scale, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t k, float sm_scale, void* out,
+                      int32_t out_dtype, int32_t* sel_opt, int32_t* n_sel_opt, int32_t* pos_opt,
+                      int32_t* n_pos_opt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QSA_H */
