@@ -22,7 +22,7 @@ WsLayout ws_layout(int num_q, int max_blocks, int hq, int hkv, int k) {
   WsLayout w;
   const int width = QSA_BLOCK * k + QSA_BLOCK - 1;
   size_t off = 0;
-  w.counters = off; off += align_up((size_t)num_q * hkv * sizeof(uint32_t));
+  w.counters = off; off += align_up((size_t)num_q * hkv * qsa::kCounterStride * sizeof(uint32_t));
   w.partials = off; off += align_up(qsa::attn_partial_bytes(num_q, hkv, hq / hkv, width));
   w.attn_end = off;
   w.scores = off; off += align_up((size_t)num_q * (size_t)(max_blocks > 0 ? max_blocks : 1) * sizeof(float));
@@ -39,7 +39,7 @@ qsa_status check_batch(const qsa_batch* b) {
   if (!b->q_start || !b->seq_len || !b->kv_start || !b->blk_start) return QSA_ERR_NULL;
   if (b->num_req < 1 || b->num_req > QSA_MAX_REQUESTS) return QSA_ERR_SHAPE;
   if (b->num_q < b->num_req || b->num_q > QSA_MAX_Q_PER_REQ * b->num_req) return QSA_ERR_SHAPE;
-  if (b->max_blocks < 0 || b->max_blocks > (1 << 28)) return QSA_ERR_SHAPE;
+  if (b->max_blocks < 0 || b->max_blocks > QSA_MAX_BLOCKS) return QSA_ERR_SHAPE;
   return QSA_OK;
 }
 

@@ -9,7 +9,8 @@
 // 32 gathered positions per step and serves the whole GQA group of that KV
 // head (up to 16 query heads) at once on bf16 MFMA 16x16x32:
 //   S^T[pos][head] = K[pos][:] . Q[head][:]      (2 tiles x 4 MFMAs)
-//   O^T[dim][head] += V^T[dim][pos] P^T[pos][head]  (8 MFMAs)
+//   O^T[dim][head] += V^T[dim][pos] P^T[pos][head]  (8 MFMAs each for the BF16
+//                                                    high and low parts of P)
 // The GQA group is the 16-column side of the tile; the gathered positions
 // are the dense side.  The position order inside the k dimension of the PV
 // product is chosen so that each lane's P values come straight out of the
@@ -22,7 +23,9 @@
 // Softmax is online per wave (running max and sum in the log2 domain), the 4
 // waves of a workgroup merge in LDS, and when a unit is split over several
 // workgroups the last one to finish merges the partials (an arrival counter
-// in the workspace, reset to zero by that last workgroup).
+// in the workspace, one 128-byte line per unit, reset to zero by that last
+// workgroup).  Partials travel through device-coherent stores and loads, so
+// the hand-off needs no cache flush or invalidation.
 #include "qsa_common.hpp"
 #include "qsa_launch.hpp"
 
@@ -70,7 +73,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   constexpr int EB = kFp8 ? 1 : 2;            // bytes per KV element
   __shared__ float o_s[kAttnWaves][16][kOStride];
   __shared__ float m_s[kAttnWaves][16], l_s[kAttnWaves][16];
-  __shared__ float w_s[64];
+  __shared__ float w_s[16];
+  __shared__ float ml_s[kMaxSplits][32];
   __shared__ int s_last;
 
   const int q = blockIdx.x, s = blockIdx.y, g = blockIdx.z;
@@ -183,16 +187,20 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
     const float m_new = fmaxf(m_run, mloc);
     const float alpha = exp2f(m_run - m_new);
-    uint32_t pw[4];
+    // P = P_hi + P_lo, both BF16: the PV product then carries ~16 bits of P.
+    uint32_t ph[4], plo[4];
     float psum = 0.f;
 #pragma unroll
     for (int e2 = 0; e2 < 4; ++e2) {
-      pw[e2] = pack_bf16x2(exp2f(sv[2 * e2] - m_new), exp2f(sv[2 * e2 + 1] - m_new));
-      psum += bf16lo_to_f32(pw[e2]) + bf16hi_to_f32(pw[e2]);
+      const float p0 = exp2f(sv[2 * e2] - m_new), p1 = exp2f(sv[2 * e2 + 1] - m_new);
+      ph[e2] = pack_bf16x2(p0, p1);
+      plo[e2] = pack_bf16x2(p0 - bf16lo_to_f32(ph[e2]), p1 - bf16hi_to_f32(ph[e2]));
+      psum += p0 + p1;
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+    const bf16x8 pb_hi = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
+    const bf16x8 pb_lo = __builtin_bit_cast(bf16x8, u32x4{plo[0], plo[1], plo[2], plo[3]});
 
     // O^T += V^T P^T; tile u covers dims 8i + u for accumulator row i.
 #pragma unroll
@@ -203,8 +211,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
       a.y = perm_b32(vr[3][u >> 1], vr[2][u >> 1], selb);
       a.z = perm_b32(vr[5][u >> 1], vr[4][u >> 1], selb);
       a.w = perm_b32(vr[7][u >> 1], vr[6][u >> 1], selb);
+      const bf16x8 va = __builtin_bit_cast(bf16x8, a);
       o[u] = o[u] * alpha;
-      o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pb, o[u], 0, 0, 0);
+      o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb_hi, o[u], 0, 0, 0);
+      o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb_lo, o[u], 0, 0, 0);
     }
   }
 
@@ -249,11 +259,15 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
     return;
   }
 
-  // Split partial: [G*128 unnormalised O][16 m][16 l] per (q, g, s).
+  // Split partial: [G*128 unnormalised O][16 m][16 l] per (q, g, s), published
+  // with device-coherent (write-through) stores: no cache flush is needed
+  // before the arrival is counted, only the stores' completion.
   const int pstride = G * D + 32;
   float* unit = p.part + ((int64_t)q * Hkv + g) * p.splits * pstride;
   float* mine = unit + (int64_t)s * pstride;
   for (int idx = tid; idx < nout + 2 * G; idx += blockDim.x) {
+    float val;
+    int dst;
     if (idx < nout) {
       const int hh = idx / D, d = idx % D;
       float M = -INFINITY;
@@ -263,7 +277,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
 #pragma unroll
       for (int w = 0; w < kAttnWaves; ++w)
         num += (m_s[w][hh] == -INFINITY ? 0.f : exp2f(m_s[w][hh] - M)) * o_s[w][hh][d];
-      mine[idx] = num;
+      val = num;
+      dst = idx;
     } else {
       const int hh = (idx - nout) % G;
       const bool is_l = (idx - nout) >= G;
@@ -271,56 +286,67 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
 #pragma unroll
       for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, m_s[w][hh]);
       if (!is_l) {
-        mine[nout + hh] = M;
+        val = M;
+        dst = nout + hh;
       } else {
         float den = 0.f;
 #pragma unroll
         for (int w = 0; w < kAttnWaves; ++w)
           den += (m_s[w][hh] == -INFINITY ? 0.f : exp2f(m_s[w][hh] - M)) * l_s[w][hh];
-        mine[nout + 16 + hh] = den;
+        val = den;
+        dst = nout + 16 + hh;
       }
     }
+    __hip_atomic_store(mine + dst, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);     // this thread's stores have reached the coherence point
   __syncthreads();
   if (tid == 0) {
-    const uint32_t ticket = atomicAdd(&p.counters[q * Hkv + g], 1u);
+    const uint32_t ticket = atomicAdd(&p.counters[(q * Hkv + g) * kCounterStride], 1u);
     s_last = ticket == (uint32_t)(p.splits - 1);
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
-  // Last workgroup of the unit: merge all splits.  w_s[hh] = 1 / denominator,
-  // then each output element sums the splits' rescaled numerators.
+  // Last workgroup of the unit: merge all splits with device-coherent loads.
   const int S = p.splits;
+  for (int i = tid; i < S * 2 * G; i += blockDim.x) {
+    const int t = i / (2 * G), r = i % (2 * G);
+    const int off = r < G ? nout + r : nout + 16 + (r - G);
+    ml_s[t][r] = __hip_atomic_load(unit + (int64_t)t * pstride + off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
   if (tid < G) {
     float M = -INFINITY;
-    for (int t = 0; t < S; ++t) M = fmaxf(M, __builtin_nontemporal_load(unit + (int64_t)t * pstride + nout + tid));
+    for (int t = 0; t < S; ++t) M = fmaxf(M, ml_s[t][tid]);
     float den = 0.f;
     for (int t = 0; t < S; ++t) {
-      const float mt = __builtin_nontemporal_load(unit + (int64_t)t * pstride + nout + tid);
-      if (mt != -INFINITY)
-        den += exp2f(mt - M) * __builtin_nontemporal_load(unit + (int64_t)t * pstride + nout + 16 + tid);
+      const float mt = ml_s[t][tid];
+      const float wgt = mt == -INFINITY ? 0.f : exp2f(mt - M);
+      ml_s[t][tid] = wgt;                       // weight of split t for head tid
+      den += wgt * ml_s[t][G + tid];
     }
-    w_s[tid] = M;
-    w_s[32 + tid] = 1.f / den;
+    w_s[tid] = vscale / den;
   }
   __syncthreads();
   for (int idx = tid; idx < nout; idx += blockDim.x) {
     const int hh = idx / D;
-    const float M = w_s[hh];
+    float vals[kMaxSplits];
+#pragma unroll
+    for (int t = 0; t < kMaxSplits; ++t)
+      vals[t] = t < S ? __hip_atomic_load(unit + (int64_t)t * pstride + idx, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT)
+                      : 0.f;
     float num = 0.f;
-    for (int t = 0; t < S; ++t) {
-      const float mt = __builtin_nontemporal_load(unit + (int64_t)t * pstride + nout + hh);
-      if (mt != -INFINITY) num += exp2f(mt - M) * __builtin_nontemporal_load(unit + (int64_t)t * pstride + idx);
-    }
-    const float val = num * w_s[32 + hh] * vscale;
+#pragma unroll
+    for (int t = 0; t < kMaxSplits; ++t)
+      if (t < S) num += ml_s[t][hh] * vals[t];
+    const float val = num * w_s[hh];
     const int64_t oi = ((int64_t)q * Hq + g * G) * D + idx;
     if (kOutBf16) static_cast<__bf16*>(p.out)[oi] = (__bf16)val;
     else static_cast<float*>(p.out)[oi] = val;
   }
-  if (tid == 0) p.counters[q * Hkv + g] = 0u;
+  if (tid == 0) p.counters[(q * Hkv + g) * kCounterStride] = 0u;
 }
 
 size_t attn_partial_bytes(int num_q, int num_kv_heads, int group, int width) {

@@ -19,6 +19,8 @@ constexpr int kChunk = 32;             // positions per attention step of one wa
 constexpr int kAttnWaves = 4;          // waves per attention workgroup
 constexpr int kSelectThreads = 1024;   // threads of one top-k workgroup
 constexpr int kRadixBins = 2048;       // 11-bit digits: passes over bits 31..21, 20..10, 9..0
+constexpr int kMaxSplits = (QSA_WIDTH + kChunk * kAttnWaves - 1) / (kChunk * kAttnWaves);  // 17
+constexpr int kCounterStride = 32;     // uint32 words per arrival counter (one 128-byte line)
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
@@ -54,36 +56,41 @@ __device__ __forceinline__ float fdot2_bf16(uint32_t a, uint32_t b, float c) {
                                          c, false);
 }
 
-// Wave-wide inclusive prefix sum of unsigned values.
+// Wave-wide inclusive prefix sum of unsigned values: a DPP shift-scan inside
+// each 16-lane row (lanes shifted in from outside the row read 0), then the
+// row totals are added through lane reads.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    uint32_t t = __shfl_up(v, off, kWave);
-    if (lane >= off) v += t;
-  }
-  return v;
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const int row = lane_id() >> 4;
+  return v + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
 }
 
 // Block-wide exclusive prefix sum for blockDim.x == NT (multiple of 64).
-// `scratch` needs NT/64 + 1 words of LDS.  Returns the exclusive prefix of
-// this thread and writes the block total to *total.  Contains two barriers.
+// `scratch` needs NT/64 words of LDS.  Returns this thread's exclusive prefix
+// and the block total.  One barrier inside; the caller must separate two
+// calls that share `scratch` by a barrier.
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
   constexpr int NW = NT / kWave;
   const int lane = lane_id(), wave = threadIdx.x / kWave;
-  uint32_t inc = wave_inclusive_scan(v);
+  const uint32_t inc = wave_inclusive_scan(v);
   if (lane == kWave - 1) scratch[wave] = inc;
   __syncthreads();
-  if (wave == 0) {
-    uint32_t w = lane < NW ? scratch[lane] : 0u;
-    uint32_t wi = wave_inclusive_scan(w);
-    if (lane < NW) scratch[lane] = wi - w;
-    if (lane == NW - 1) scratch[NW] = wi;
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t t = scratch[w];
+    before += w < wave ? t : 0u;
+    all += t;
   }
-  __syncthreads();
-  *total = scratch[NW];
-  return scratch[wave] + inc - v;
+  *total = all;
+  return before + inc - v;
 }
 
 // Attention split geometry shared by the launcher and the workspace sizing.
@@ -97,7 +104,7 @@ __host__ __device__ inline AttnSplit attn_split(int num_q, int num_kv_heads, int
   const int units = num_q * num_kv_heads;
   const int target_wgs = 1024;
   int splits = (target_wgs + units - 1) / units;
-  int max_splits = (chunks + kAttnWaves - 1) / kAttnWaves;
+  int max_splits = (chunks + kAttnWaves - 1) / kAttnWaves;   // <= kMaxSplits for width <= QSA_WIDTH
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
   int cps = (chunks + splits - 1) / splits;

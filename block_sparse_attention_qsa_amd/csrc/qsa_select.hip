@@ -9,18 +9,73 @@
 //
 // One 1024-thread workgroup handles one query:
 //   1. FP32 scores -> order-preserving uint32 keys (-0.0 folded onto +0.0),
-//      staged in LDS when they fit (else re-read from the L2-resident buffer).
+//      staged in LDS when they fit.
 //   2. Three MSB-first radix passes (11, 11, 10 bits) with LDS histograms find
 //      the key T of the k-th best block and how many blocks equal to T to keep.
-//   3. An ordered compaction (two block scans over contiguous per-thread
-//      segments) keeps every key > T and the lowest-index keys == T, so ties go
-//      to the lower block index and the output comes out in ascending order.
+//   3. An ordered compaction (one packed block scan over contiguous
+//      per-thread segments) keeps every key > T and the lowest-index keys == T,
+//      so ties go to the lower block index and the output is ascending.
+// Scans are DPP shift-scans inside each 16-lane row; the bucket search after a
+// histogram pass is done by a single wave.  When the keys do not fit in LDS,
+// the first pass streams the score buffer and only the keys falling in the
+// chosen top-level bin are staged for the remaining passes.
 #include "qsa_common.hpp"
 #include "qsa_launch.hpp"
 
 namespace qsa {
 
-constexpr int kKeyCap = 16384;   // keys staged in LDS (64 KiB)
+constexpr int kKeyCap = 32768;   // keys staged in LDS (128 KiB of the 160 KiB a workgroup may use)
+constexpr int kBatch = 8;        // loads a thread keeps in flight while streaming scores
+
+// Histogram increment for a wave: when every active lane carries the same
+// bin (long runs of tied scores) one lane adds the whole count.
+__device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool active) {
+  const uint64_t act = __ballot(active);
+  if (act == 0) return;
+  const int first = __builtin_ctzll(act);
+  const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)bin, first);
+  if (__ballot(active && bin != b0) == 0) {
+    if (lane_id() == first) atomicAdd(&hist[b0], (uint32_t)__popcll(act));
+  } else if (active) {
+    atomicAdd(&hist[bin], 1u);
+  }
+}
+
+// One wave scans hist[2047 .. 0] from the top and finds the bin where the
+// running count first reaches krem; that lane stores the refined prefix and
+// the count still to take inside the bin and the bin's population.  Lane l
+// owns bins 2016-32l .. 2047-32l.
+__device__ __forceinline__ void find_bucket(const uint32_t* hist, uint32_t krem, uint32_t prefix, int shift,
+                                            uint32_t* s_prefix, uint32_t* s_krem, uint32_t* s_count) {
+  const int lo = kRadixBins - 32 - 32 * lane_id();
+  uint32_t c[32];
+  const u32x4* h4 = reinterpret_cast<const u32x4*>(hist + lo);
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const u32x4 x = h4[v];
+    c[4 * v + 0] = x.x;
+    c[4 * v + 1] = x.y;
+    c[4 * v + 2] = x.z;
+    c[4 * v + 3] = x.w;
+  }
+  uint32_t sum = 0;
+#pragma unroll
+  for (int b = 0; b < 32; ++b) sum += c[b];
+  const uint32_t inc = wave_inclusive_scan(sum);
+  const uint32_t exc = inc - sum;
+  if (exc < krem && krem <= inc) {
+    uint32_t run = exc;
+#pragma unroll
+    for (int b = 31; b >= 0; --b) {
+      if (run < krem && krem <= run + c[b]) {
+        *s_prefix = prefix | ((uint32_t)(lo + b) << shift);
+        *s_krem = krem - run;
+        *s_count = c[b];
+      }
+      run += c[b];
+    }
+  }
+}
 
 template <bool kWritePos>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(Meta m, const float* __restrict__ scores,
@@ -31,11 +86,11 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Meta m, const fl
   constexpr int NT = kSelectThreads;
   __shared__ uint32_t keys_lds[kKeyCap];
   __shared__ uint32_t hist[kRadixBins];
-  __shared__ uint32_t scan_scratch[NT / kWave + 1];
-  __shared__ uint32_t s_prefix, s_krem;
+  __shared__ uint32_t scan_scratch[NT / kWave];
+  __shared__ uint32_t s_prefix, s_krem, s_count, s_ncand;
 
   const int q = blockIdx.x;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const int r = request_of(m.q_start, m.num_req, q);
   const int qs = m.q_start[r];
   const int nq = m.q_start[r + 1] - qs;
@@ -62,11 +117,30 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Meta m, const fl
     return;
   }
 
-  const bool in_lds = nf <= kKeyCap;
-  if (in_lds)
-    for (int i = tid; i < nf; i += NT) keys_lds[i] = score_key(srow[i]);
-  auto key_at = [&](int i) -> uint32_t { return in_lds ? keys_lds[i] : score_key(srow[i]); };
+  // ---- 1. keys.  All nf keys go to LDS when they fit; otherwise the first
+  // radix pass streams the score buffer and only the keys of the chosen
+  // top-level bin are staged for the later passes.
+  const bool staged = nf <= kKeyCap;
+  if (staged) {
+#pragma unroll
+    for (int b = 0; b < kKeyCap / NT; b += kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int i = (b + u) * NT + tid;
+        v[u] = i < nf ? srow[i] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int i = (b + u) * NT + tid;
+        if (i < nf) keys_lds[i] = score_key(v[u]);
+      }
+    }
+  }
 
+  // ---- 2. MSB-first radix passes over 11, 11 and 10 bits.
+  int nkeys = staged ? nf : 0;
+  bool from_lds = staged;
   uint32_t prefix = 0u, pmask = 0u, krem = (uint32_t)k;
 #pragma unroll 1
   for (int pass = 0; pass < 3; ++pass) {
@@ -74,59 +148,125 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(Meta m, const fl
     const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
     for (int i = tid; i < kRadixBins; i += NT) hist[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < nf; i += NT) {
-      const uint32_t key = key_at(i);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+    if (from_lds) {
+      for (int i0 = 0; i0 < nkeys; i0 += NT) {
+        const int i = i0 + tid;
+        const uint32_t key = i < nkeys ? keys_lds[i] : 0u;
+        hist_add(hist, (key >> shift) & dmask, i < nkeys && (key & pmask) == prefix);
+      }
+    } else {
+      for (int base = 0; base < nf; base += NT * kBatch) {
+        float v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int i = base + u * NT + tid;
+          v[u] = i < nf ? srow[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int i = base + u * NT + tid;
+          const uint32_t key = score_key(v[u]);
+          hist_add(hist, (key >> shift) & dmask, i < nf && (key & pmask) == prefix);
+        }
+      }
     }
     __syncthreads();
-    // thread t owns bins 2047-2t (upper) and 2046-2t (lower); scan from the top
-    const int bu = kRadixBins - 1 - 2 * tid;
-    const uint32_t hu = hist[bu], hl = hist[bu - 1];
-    uint32_t tot;
-    const uint32_t above = block_exclusive_scan<NT>(hu + hl, scan_scratch, &tot);
-    if (above < krem && krem <= above + hu) {
-      s_prefix = prefix | ((uint32_t)bu << shift);
-      s_krem = krem - above;
-    } else if (above + hu < krem && krem <= above + hu + hl) {
-      s_prefix = prefix | ((uint32_t)(bu - 1) << shift);
-      s_krem = krem - above - hu;
-    }
+    if (wave == 0) find_bucket(hist, krem, prefix, shift, &s_prefix, &s_krem, &s_count);
+    if (tid == 0) s_ncand = 0u;
     __syncthreads();
+    // every thread reads the shared results of this pass before any thread can
+    // reach the next pass (which clears hist and rewrites them after a barrier)
     prefix = s_prefix;
     krem = s_krem;
+    const uint32_t bin_count = s_count;
     pmask |= dmask << shift;
+    if (!from_lds && bin_count <= (uint32_t)kKeyCap) {
+      // stage the keys of the chosen top-level bin (wave-aggregated append)
+      for (int base = 0; base < nf; base += NT * kBatch) {
+        float v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int i = base + u * NT + tid;
+          v[u] = i < nf ? srow[i] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int i = base + u * NT + tid;
+          const uint32_t key = score_key(v[u]);
+          const bool mine = i < nf && (key & pmask) == prefix;
+          const uint64_t bal = __ballot(mine);
+          if (bal) {
+            uint32_t wbase = 0;
+            if (lane == 0) wbase = atomicAdd(&s_ncand, (uint32_t)__popcll(bal));
+            wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase);
+            const uint32_t rank =
+                __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (mine) keys_lds[wbase + rank] = key;
+          }
+        }
+      }
+      __syncthreads();
+      nkeys = (int)s_ncand;
+      from_lds = true;
+    }
   }
   const uint32_t T = prefix;        // key of the k-th best block
   const uint32_t need_eq = krem;    // blocks equal to T that are kept (lowest indices first)
 
+  // ---- 3. ordered compaction over contiguous per-thread segments [beg, end):
+  // one packed scan gives, before this thread, the count of keys > T (high
+  // 12 bits) and of keys == T (low 20 bits); the kept keys before it are
+  // gt_before + min(eq_before, need_eq).
   const int E = (nf + NT - 1) / NT;
   const int beg = min(tid * E, nf), end = min(beg + E, nf);
-  uint32_t eq = 0;
-  for (int i = beg; i < end; ++i) eq += key_at(i) == T;
-  uint32_t tot;
-  const uint32_t eq_before = block_exclusive_scan<NT>(eq, scan_scratch, &tot);
-  uint32_t cnt = 0, seen = eq_before;
-  for (int i = beg; i < end; ++i) {
-    const uint32_t key = key_at(i);
-    if (key > T) ++cnt;
-    else if (key == T) { cnt += seen < need_eq; ++seen; }
+  uint32_t gt = 0, eq = 0;
+  for (int i0 = beg; i0 < end; i0 += kBatch) {
+    uint32_t kk[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u;
+      kk[u] = i < end ? (staged ? keys_lds[i] : score_key(srow[i])) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      gt += (i0 + u < end) && kk[u] > T;
+      eq += (i0 + u < end) && kk[u] == T;
+    }
   }
-  uint32_t o = block_exclusive_scan<NT>(cnt, scan_scratch, &tot);
-  seen = eq_before;
-  for (int i = beg; i < end; ++i) {
-    const uint32_t key = key_at(i);
-    bool take = key > T;
-    if (key == T) { take = seen < need_eq; ++seen; }
-    if (take) {
-      sel_row[o] = i;
-      if (kWritePos) {
-        const int p0 = kv0 + 4 * i;
-        pos_row[4 * o + 0] = p0;
-        pos_row[4 * o + 1] = p0 + 1;
-        pos_row[4 * o + 2] = p0 + 2;
-        pos_row[4 * o + 3] = p0 + 3;
+  uint32_t tot;
+  const uint32_t before = block_exclusive_scan<NT>((gt << 20) | eq, scan_scratch, &tot);
+  const uint32_t eq_before = before & 0xFFFFFu;
+  uint32_t o = (before >> 20) + min(eq_before, need_eq);
+  uint32_t seen = eq_before;
+  for (int i0 = beg; i0 < end; i0 += kBatch) {
+    uint32_t kk[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u;
+      kk[u] = i < end ? (staged ? keys_lds[i] : score_key(srow[i])) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u;
+      bool take = false;
+      if (i < end) {
+        take = kk[u] > T;
+        if (kk[u] == T) {
+          take = seen < need_eq;
+          ++seen;
+        }
       }
-      ++o;
+      if (take) {
+        sel_row[o] = i;
+        if (kWritePos) {
+          const int p0 = kv0 + 4 * i;
+          pos_row[4 * o + 0] = p0;
+          pos_row[4 * o + 1] = p0 + 1;
+          pos_row[4 * o + 2] = p0 + 2;
+          pos_row[4 * o + 3] = p0 + 3;
+        }
+        ++o;
+      }
     }
   }
   if (kWritePos) {

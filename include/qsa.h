@@ -55,7 +55,8 @@ extern "C" {
 #define QSA_HEAD_DIM 128                             /* attention head dim                */
 #define QSA_MAX_Q_PER_REQ 4                          /* verify queries sharing a key load */
 #define QSA_MAX_GQA_GROUP 16                         /* query heads per KV head           */
-#define QSA_MAX_REQUESTS 65536
+#define QSA_MAX_REQUESTS 16384                       /* num_q <= 4 * 16384 = 65536     */
+#define QSA_MAX_BLOCKS (1 << 20)                     /* full blocks per request (4M tokens) */
 
 typedef enum {
   QSA_OK = 0,
@@ -73,7 +74,7 @@ typedef enum { QSA_OUT_F32 = 0, QSA_OUT_BF16 = 1 } qsa_out_dtype;
 typedef struct {
   int32_t num_req;           /* [host] B >= 1                                          */
   int32_t num_q;             /* [host] total queries = q_start[B]                      */
-  int32_t max_blocks;        /* [host] >= max over r of seq_len[r] / 4                 */
+  int32_t max_blocks;        /* [host] >= max over r of seq_len[r] / 4, <= QSA_MAX_BLOCKS */
   const int32_t* q_start;    /* [dev]  int32[B+1], q_start[0] = 0, 1..4 queries each  */
   const int32_t* seq_len;    /* [dev]  int32[B], cached tokens incl. verify tokens     */
   const int32_t* kv_start;   /* [dev]  int32[B], first KV slot of request r            */

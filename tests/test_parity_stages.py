@@ -77,13 +77,18 @@ def _select_case(nfs, kind, seed):
             s = rng.choice(np.array([-0.0, 0.0, 1.0, -1.0], np.float32), nf)
         elif kind == "wide":
             s = (rng.standard_normal(nf) * 10.0 ** rng.integers(-30, 30, nf)).astype(np.float32)
+        elif kind == "flat":
+            # 60% of the blocks share the top score: the chosen top-level radix
+            # bin can exceed what the selector stages in LDS
+            s = rng.uniform(-3.0, 2.0, nf).astype(np.float32)
+            s[rng.random(nf) < 0.6] = 2.5
         else:
             raise ValueError(kind)
         rows.append(s)
     return rows
 
 
-@pytest.mark.parametrize("kind", ["ties", "normal", "zeros", "wide"])
+@pytest.mark.parametrize("kind", ["ties", "normal", "zeros", "wide", "flat"])
 def test_select_bit_exact(kind):
     need_gpu()
     nfs = [0, 1, 511, 512, 513, 1000, 2048, 12500, 16384, 16385, 40000, 65536]
@@ -188,7 +193,7 @@ def test_decode_small_mixed():
         assert_selection_equal(got, ref)
         assert_out_close(got["out"], ref["out"])
         # split-arrival counters sit at the start of the workspace and are reset by the call
-        assert int(got["ws"][:w.num_q * w.num_kv_heads * 4].sum()) == 0
+        assert int(got["ws"][:w.num_q * w.num_kv_heads * 128].sum()) == 0
 
 
 def test_decode_edge_lengths_dense_equivalence():
