@@ -18,6 +18,10 @@ struct WsLayout {
   size_t counters, partials, attn_end, scores, sel, n_sel, pos, n_pos, total;
 };
 
+// Row stride of the workspace score buffer: a multiple of 4 floats so that
+// score rows are 16-byte aligned.
+inline int64_t score_ld(int max_blocks) { return ((int64_t)(max_blocks > 0 ? max_blocks : 1) + 3) & ~(int64_t)3; }
+
 WsLayout ws_layout(int num_q, int max_blocks, int hq, int hkv, int k) {
   WsLayout w;
   const int width = QSA_BLOCK * k + QSA_BLOCK - 1;
@@ -25,7 +29,7 @@ WsLayout ws_layout(int num_q, int max_blocks, int hq, int hkv, int k) {
   w.counters = off; off += align_up((size_t)num_q * hkv * qsa::kCounterStride * sizeof(uint32_t));
   w.partials = off; off += align_up(qsa::attn_partial_bytes(num_q, hkv, hq / hkv, width));
   w.attn_end = off;
-  w.scores = off; off += align_up((size_t)num_q * (size_t)(max_blocks > 0 ? max_blocks : 1) * sizeof(float));
+  w.scores = off; off += align_up((size_t)num_q * (size_t)score_ld(max_blocks) * sizeof(float));
   w.sel = off; off += align_up((size_t)num_q * k * sizeof(int32_t));
   w.n_sel = off; off += align_up((size_t)num_q * sizeof(int32_t));
   w.pos = off; off += align_up((size_t)num_q * width * sizeof(int32_t));
@@ -196,7 +200,7 @@ qsa_status qsa_decode(const qsa_batch* batch, const void* idx_q, const void* cke
   int32_t* pos = pos_opt ? pos_opt : reinterpret_cast<int32_t*>(base + w.pos);
   int32_t* n_pos = n_pos_opt ? n_pos_opt : reinterpret_cast<int32_t*>(base + w.n_pos);
   const Meta m = meta_of(batch);
-  const int64_t ld = batch->max_blocks > 0 ? batch->max_blocks : 1;
+  const int64_t ld = score_ld(batch->max_blocks);
 
   QSA_TRY(launched(qsa::launch_score(m, idx_q, ckeys, scores, ld, stream)));
   QSA_TRY(launched(qsa::launch_select(m, scores, ld, k, sel, n_sel, pos, n_pos, width, stream)));

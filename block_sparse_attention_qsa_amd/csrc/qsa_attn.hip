@@ -5,7 +5,8 @@
 // BF16 queries and BF16 or FP8 E4M3 KV.  This is a gfx950 design for the same
 // contract.
 //
-// Work unit: (query, split of the position buffer, KV head) = grid (x, y, z).  A wave takes
+// Work unit: (query, split of the position buffer, KV head), query fastest in
+// the 1-D grid.  A wave takes
 // 32 gathered positions per step and serves the whole GQA group of that KV
 // head (up to 16 query heads) at once on bf16 MFMA 16x16x32:
 //   S^T[pos][head] = K[pos][:] . Q[head][:]      (2 tiles x 4 MFMAs)
@@ -20,7 +21,8 @@
 // hardware converter; the per-head K scale folds into the softmax scale and
 // the V scale into the final normalisation.
 //
-// Softmax is online per wave (running max and sum in the log2 domain), the 4
+// Softmax is online per wave (running reference max, moved lazily, and sum in
+// the log2 domain), the 4
 // waves of a workgroup merge in LDS, and when a unit is split over several
 // workgroups the last one to finish merges the partials (an arrival counter
 // in the workspace, one 128-byte line per unit, reset to zero by that last
@@ -32,6 +34,8 @@
 namespace qsa {
 
 constexpr int kOStride = QSA_HEAD_DIM + 4;   // padded LDS row of one head's output
+constexpr int kMaxHeads = 8 * ((QSA_WIDTH + kChunk - 1) / kChunk);   // block heads of one split
+constexpr float kRescaleSlack = 8.f;     // log2 headroom of the softmax reference maximum
 
 struct AttnParams {
   const uint16_t* q;
@@ -67,31 +71,195 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+template <bool kFp8> struct VRaw { typedef u32x4 type; };   // 8 BF16 of one V row
+template <> struct VRaw<true> { typedef u32x2 type; };      // 8 FP8 of one V row
+
+// Raw K/V bytes of one 32-position chunk as one lane holds them.
+template <bool kFp8>
+struct ChunkRaw {
+  u32x4 k[2][kFp8 ? 2 : 4];             // K rows 16t + j: dims kg*32 .. kg*32+31
+  typename VRaw<kFp8>::type v[8];       // V rows 16t + 4kg + rr (e = 4t + rr): dims 8j .. 8j+7
+  uint32_t vmask;                       // bit e: V / score position e holds a valid slot
+};
+
+// Block heads of one chunk: the position buffer is made of runs of 4
+// consecutive slots (one 4-token block each), so entry i is head(i & ~3) + (i & 3).
+struct ChunkHeads {
+  int k[2];   // heads of the blocks holding K rows 16t + j
+  int v[2];   // heads of the blocks holding V rows 16t + 4kg + rr
+};
+
+// Block heads of chunk c from the workgroup's LDS copy (heads_s[8 * (c - c0) + b]
+// is the slot of position 32c + 4b).  LDS reads do not join the in-order
+// vector-memory counter, so they never force a wait on K/V loads in flight.
+__device__ __forceinline__ ChunkHeads lds_heads(const int* heads_s, int c_rel, int cps, int j, int kg) {
+  ChunkHeads h;
+  c_rel = min(c_rel, cps - 1);          // chunks past the split only issue masked loads
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    h.k[t] = heads_s[8 * c_rel + 4 * t + (j >> 2)];
+    h.v[t] = heads_s[8 * c_rel + 4 * t + kg];
+  }
+  return h;
+}
+
+// Issue the K/V loads of the chunk starting at position `base`.  Positions at
+// or past `npos` (all of them when the chunk is past the end) read the first
+// slot instead and are masked out, so the issue never needs a branch.
+template <bool kFp8>
+__device__ __forceinline__ void issue_chunk(ChunkRaw<kFp8>& ch, const ChunkHeads& h, int base, int npos, int slot0,
+                                            const uint8_t* kbase, const uint8_t* vbase, uint32_t row_stride, int j,
+                                            int kg) {
+  constexpr int EB = kFp8 ? 1 : 2;
+  const uint8_t* kl = kbase + kg * 32 * EB;   // this lane's bytes inside a K row
+  const uint8_t* vl = vbase + j * 8 * EB;     // and inside a V row
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int i = base + 16 * t + j;
+    const uint32_t slot = (uint32_t)(i < npos ? h.k[t] + (j & 3) : slot0);
+    const uint8_t* kr = kl + (uint64_t)slot * row_stride;
+#pragma unroll
+    for (int w = 0; w < (kFp8 ? 2 : 4); ++w) ch.k[t][w] = *reinterpret_cast<const u32x4*>(kr + 16 * w);
+  }
+  uint32_t vm = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int t = e >> 2, rr = e & 3;
+    const int i = base + 16 * t + 4 * kg + rr;
+    const bool valid = i < npos;
+    vm |= (uint32_t)valid << e;
+    const uint32_t slot = (uint32_t)(valid ? h.v[t] + rr : slot0);
+    ch.v[e] = *reinterpret_cast<const typename VRaw<kFp8>::type*>(vl + (uint64_t)slot * row_stride);
+  }
+  ch.vmask = vm;
+}
+
+template <bool kFp8>
+__device__ __forceinline__ void compute_chunk(const ChunkRaw<kFp8>& ch, const bf16x8 (&qb)[4], float sl2,
+                                              float& m_run, float& l_run, f32x4 (&o)[8]) {
+  // K operand (A): lane holds dims kg*32 .. kg*32+31 of its row, as 4 x 8 bf16.
+  bf16x8 ka[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (kFp8) {
+      const uint32_t ws[8] = {ch.k[t][0].x, ch.k[t][0].y, ch.k[t][0].z, ch.k[t][0].w,
+                              ch.k[t][kFp8 ? 1 : 0].x, ch.k[t][kFp8 ? 1 : 0].y, ch.k[t][kFp8 ? 1 : 0].z,
+                              ch.k[t][kFp8 ? 1 : 0].w};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const u32x2 lo = fp8x4_to_bf16x4(ws[2 * kk]), hi = fp8x4_to_bf16x4(ws[2 * kk + 1]);
+        ka[t][kk] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) ka[t][kk] = __builtin_bit_cast(bf16x8, ch.k[t][kk & (kFp8 ? 1 : 3)]);
+    }
+  }
+  // V rows as 8 bf16 each.
+  u32x4 vr[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if constexpr (kFp8) {
+      const u32x2 lo = fp8x4_to_bf16x4(ch.v[e].x), hi = fp8x4_to_bf16x4(ch.v[e].y);
+      vr[e] = u32x4{lo.x, lo.y, hi.x, hi.y};
+    } else {
+      vr[e] = ch.v[e];
+    }
+  }
+
+  // S^T = K Q^T: accumulator row kg*4 + rr = position 16t + 4kg + rr, column j = head.
+  f32x4 sacc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][kk], qb[kk], sacc[t], 0, 0, 0);
+  }
+  float sv[8];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    sv[e] = ((ch.vmask >> e) & 1u) ? sacc[e >> 2][e & 3] * sl2 : -INFINITY;
+    mloc = fmaxf(mloc, sv[e]);
+  }
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+  // Lazy rescaling: the reference maximum only moves when a score exceeds it by
+  // more than 2^kRescaleSlack, so weights stay <= 2^kRescaleSlack and the O
+  // accumulators are rescaled a handful of times per wave, not every chunk.
+  if (__ballot(mloc > m_run + kRescaleSlack)) {
+    const float m_new = fmaxf(m_run, mloc);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o[u] = o[u] * alpha;
+    m_run = m_new;
+  }
+  // P = P_hi + P_lo, both BF16: the PV product then carries ~16 bits of P.
+  uint32_t ph[4], plo[4];
+  float psum = 0.f;
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2) {
+    const float p0 = __builtin_amdgcn_exp2f(sv[2 * e2] - m_run), p1 = __builtin_amdgcn_exp2f(sv[2 * e2 + 1] - m_run);
+    ph[e2] = pack_bf16x2(p0, p1);
+    plo[e2] = pack_bf16x2(p0 - bf16lo_to_f32(ph[e2]), p1 - bf16hi_to_f32(ph[e2]));
+    psum += p0 + p1;
+  }
+  l_run += psum;
+  const bf16x8 pb_hi = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
+  const bf16x8 pb_lo = __builtin_bit_cast(bf16x8, u32x4{plo[0], plo[1], plo[2], plo[3]});
+
+  // O^T += V^T P^T; tile u covers dims 8i + u for accumulator row i.
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const uint32_t selb = (u & 1) ? 0x07060302u : 0x05040100u;
+    u32x4 a;
+    a.x = perm_b32(vr[1][u >> 1], vr[0][u >> 1], selb);
+    a.y = perm_b32(vr[3][u >> 1], vr[2][u >> 1], selb);
+    a.z = perm_b32(vr[5][u >> 1], vr[4][u >> 1], selb);
+    a.w = perm_b32(vr[7][u >> 1], vr[6][u >> 1], selb);
+    const bf16x8 va = __builtin_bit_cast(bf16x8, a);
+    o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb_hi, o[u], 0, 0, 0);
+    o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb_lo, o[u], 0, 0, 0);
+  }
+}
+
 template <bool kFp8, bool kOutBf16>
 __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   constexpr int D = QSA_HEAD_DIM;
   constexpr int EB = kFp8 ? 1 : 2;            // bytes per KV element
+  constexpr int kGroupOut = 4;                // merged outputs per thread per round
   __shared__ float o_s[kAttnWaves][16][kOStride];
   __shared__ float m_s[kAttnWaves][16], l_s[kAttnWaves][16];
   __shared__ float w_s[16];
   __shared__ float ml_s[kMaxSplits][32];
+  __shared__ int heads_s[kMaxHeads];
   __shared__ int s_last;
 
-  const int q = blockIdx.x, s = blockIdx.y, g = blockIdx.z;
+  // 1-D grid, query fastest, then split, then KV head.
+  const int Hkv = p.num_kv_heads;
+  const int num_q = (int)(gridDim.x / (unsigned)(Hkv * p.splits));
+  const int q = blockIdx.x % num_q;
+  const int s = (blockIdx.x / num_q) % p.splits;
+  const int g = blockIdx.x / (num_q * p.splits);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int j = lane & 15, kg = lane >> 4;
   const int G = p.group;
   const bool hvalid = j < G;
-  const int Hq = p.num_q_heads, Hkv = p.num_kv_heads;
-
-  const int npos = p.n_pos[q];
-  const int nchunks = (npos + kChunk - 1) / kChunk;
-  const int c_begin = s * p.cps;
-  const int c_end = min(c_begin + p.cps, nchunks);
+  const int Hq = p.num_q_heads;
   const int32_t* prow = p.pos + (int64_t)q * p.width;
-  const int slot0 = prow[0];
+  const int c0 = s * p.cps;                 // first chunk of this workgroup's split
+  const int cfirst = c0 + wave;
 
-  // Q^T as the B operand: lane (kg, j) holds head j, dims kg*32 + kk*8 + e.
+  // Prologue: the block heads of the split go to LDS (one coalesced round),
+  // together with the query, the valid length and the first slot.
+  for (int h = tid; h < 8 * p.cps; h += blockDim.x) {
+    const int i = 4 * (8 * c0 + h);
+    heads_s[h] = i < p.width ? prow[i] : 0;
+  }
+  const int npos = p.n_pos[q];
+  const int slot0 = prow[0];
   bf16x8 qb[4];
   {
     const uint16_t* qrow = p.q + ((int64_t)q * Hq + g * G + j) * D + kg * 32;
@@ -104,117 +272,50 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   const float kscale = kFp8 ? p.k_scale[g] : 1.f;
   const float vscale = kFp8 ? p.v_scale[g] : 1.f;
   const float sl2 = p.sm_scale_log2 * kscale;
-  const int64_t row_stride = (int64_t)Hkv * D * EB;   // bytes between consecutive slots
+  const uint32_t row_stride = (uint32_t)(Hkv * D * EB);   // bytes between consecutive slots
   const uint8_t* kbase = p.kc + (int64_t)g * D * EB;
   const uint8_t* vbase = p.vc + (int64_t)g * D * EB;
+  const int nchunks = (npos + kChunk - 1) / kChunk;
+  const int c_end = min(c0 + p.cps, nchunks);
+  __syncthreads();
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int c = c_begin + wave; c < c_end; c += kAttnWaves) {
-    const int base = c * kChunk;
-    // K rows: position 16t + j of the chunk; V rows: positions 16t + 4kg + rr.
-    int ks[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int idx = base + 16 * t + j;
-      const int sl = idx < npos ? prow[idx] : -1;
-      ks[t] = sl >= 0 ? sl : slot0;
+  // Main loop.  FP8: two register buffers in ping-pong, the next chunk's K/V
+  // loads are in flight while this chunk is computed.  BF16 (twice the bytes per
+  // chunk) keeps one chunk per wave in flight and relies on more waves.
+  if (kFp8) {
+    // sched_barrier keeps the compiler from sinking a chunk's loads down to
+    // its compute (which would serialise load latency and math again).
+    ChunkRaw<kFp8> ca, cb;
+    const int nl = cfirst < c_end ? npos : 0;
+    issue_chunk<kFp8>(ca, lds_heads(heads_s, cfirst - c0, p.cps, j, kg), cfirst * kChunk, nl, slot0, kbase, vbase,
+                      row_stride, j, kg);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int c = cfirst; c < c_end; c += 2 * kAttnWaves) {
+      const int cn = c + kAttnWaves;
+      issue_chunk<kFp8>(cb, lds_heads(heads_s, cn - c0, p.cps, j, kg), cn * kChunk, cn < c_end ? npos : 0, slot0,
+                        kbase, vbase, row_stride, j, kg);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_chunk<kFp8>(ca, qb, sl2, m_run, l_run, o);
+      __builtin_amdgcn_sched_barrier(0);
+      if (cn >= c_end) break;
+      const int cnn = cn + kAttnWaves;
+      issue_chunk<kFp8>(ca, lds_heads(heads_s, cnn - c0, p.cps, j, kg), cnn * kChunk, cnn < c_end ? npos : 0,
+                        slot0, kbase, vbase, row_stride, j, kg);
+      __builtin_amdgcn_sched_barrier(0);
+      compute_chunk<kFp8>(cb, qb, sl2, m_run, l_run, o);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    int vs[8];
-    bool valid[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int idx = base + 16 * (e >> 2) + 4 * kg + (e & 3);
-      const int sl = idx < npos ? prow[idx] : -1;
-      valid[e] = sl >= 0;
-      vs[e] = sl >= 0 ? sl : slot0;
-    }
-
-    // K operand (A): lane holds dims kg*32 .. kg*32+31 of its row, as 4 x 8 bf16.
-    bf16x8 ka[2][4];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint8_t* kr = kbase + (int64_t)ks[t] * row_stride + kg * 32 * EB;
-      if (kFp8) {
-        const u32x4 w0 = *reinterpret_cast<const u32x4*>(kr);
-        const u32x4 w1 = *reinterpret_cast<const u32x4*>(kr + 16);
-        const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const u32x2 lo = fp8x4_to_bf16x4(ws[2 * kk]), hi = fp8x4_to_bf16x4(ws[2 * kk + 1]);
-          ka[t][kk] = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-        }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          ka[t][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kr + kk * 16));
-      }
-    }
-    // V rows: dims 8j .. 8j+7 of each of the lane's 8 positions, as 8 bf16.
-    u32x4 vr[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint8_t* vp = vbase + (int64_t)vs[e] * row_stride + j * 8 * EB;
-      if (kFp8) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(vp);
-        const u32x2 lo = fp8x4_to_bf16x4(w.x), hi = fp8x4_to_bf16x4(w.y);
-        vr[e] = u32x4{lo.x, lo.y, hi.x, hi.y};
-      } else {
-        vr[e] = *reinterpret_cast<const u32x4*>(vp);
-      }
-    }
-
-    // S^T = K Q^T: accumulator row kg*4 + rr = position 16t + 4kg + rr, column j = head.
-    f32x4 sacc[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t][kk], qb[kk], sacc[t], 0, 0, 0);
-    }
-    float sv[8];
-    float mloc = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sv[e] = valid[e] ? sacc[e >> 2][e & 3] * sl2 : -INFINITY;
-      mloc = fmaxf(mloc, sv[e]);
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, kWave));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-    const float m_new = fmaxf(m_run, mloc);
-    const float alpha = exp2f(m_run - m_new);
-    // P = P_hi + P_lo, both BF16: the PV product then carries ~16 bits of P.
-    uint32_t ph[4], plo[4];
-    float psum = 0.f;
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      const float p0 = exp2f(sv[2 * e2] - m_new), p1 = exp2f(sv[2 * e2 + 1] - m_new);
-      ph[e2] = pack_bf16x2(p0, p1);
-      plo[e2] = pack_bf16x2(p0 - bf16lo_to_f32(ph[e2]), p1 - bf16hi_to_f32(ph[e2]));
-      psum += p0 + p1;
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    const bf16x8 pb_hi = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], ph[2], ph[3]});
-    const bf16x8 pb_lo = __builtin_bit_cast(bf16x8, u32x4{plo[0], plo[1], plo[2], plo[3]});
-
-    // O^T += V^T P^T; tile u covers dims 8i + u for accumulator row i.
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint32_t selb = (u & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 a;
-      a.x = perm_b32(vr[1][u >> 1], vr[0][u >> 1], selb);
-      a.y = perm_b32(vr[3][u >> 1], vr[2][u >> 1], selb);
-      a.z = perm_b32(vr[5][u >> 1], vr[4][u >> 1], selb);
-      a.w = perm_b32(vr[7][u >> 1], vr[6][u >> 1], selb);
-      const bf16x8 va = __builtin_bit_cast(bf16x8, a);
-      o[u] = o[u] * alpha;
-      o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb_hi, o[u], 0, 0, 0);
-      o[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb_lo, o[u], 0, 0, 0);
+  } else {
+    for (int c = cfirst; c < c_end; c += kAttnWaves) {
+      ChunkRaw<kFp8> cur;
+      issue_chunk<kFp8>(cur, lds_heads(heads_s, c - c0, p.cps, j, kg), c * kChunk, npos, slot0, kbase, vbase,
+                        row_stride, j, kg);
+      compute_chunk<kFp8>(cur, qb, sl2, m_run, l_run, o);
     }
   }
 
@@ -309,42 +410,55 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   if (!s_last) return;
 
   // Last workgroup of the unit: merge all splits with device-coherent loads.
+  // The split maxima/sums and the first round of numerators are loaded together.
   const int S = p.splits;
+  float vals[kGroupOut][kMaxSplits];
   for (int i = tid; i < S * 2 * G; i += blockDim.x) {
     const int t = i / (2 * G), r = i % (2 * G);
     const int off = r < G ? nout + r : nout + 16 + (r - G);
     ml_s[t][r] = __hip_atomic_load(unit + (int64_t)t * pstride + off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int t = 0; t < S; ++t) M = fmaxf(M, ml_s[t][tid]);
-    float den = 0.f;
-    for (int t = 0; t < S; ++t) {
-      const float mt = ml_s[t][tid];
-      const float wgt = mt == -INFINITY ? 0.f : exp2f(mt - M);
-      ml_s[t][tid] = wgt;                       // weight of split t for head tid
-      den += wgt * ml_s[t][G + tid];
+  for (int base = 0; base < nout; base += kGroupOut * blockDim.x) {
+#pragma unroll
+    for (int a = 0; a < kGroupOut; ++a) {
+      const int idx = base + a * blockDim.x + tid;
+#pragma unroll
+      for (int t = 0; t < kMaxSplits; ++t)
+        vals[a][t] = (t < S && idx < nout) ? __hip_atomic_load(unit + (int64_t)t * pstride + idx, __ATOMIC_RELAXED,
+                                                              __HIP_MEMORY_SCOPE_AGENT)
+                                           : 0.f;
     }
-    w_s[tid] = vscale / den;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < nout; idx += blockDim.x) {
-    const int hh = idx / D;
-    float vals[kMaxSplits];
+    if (base == 0) {
+      __syncthreads();
+      if (tid < G) {
+        float M = -INFINITY;
+        for (int t = 0; t < S; ++t) M = fmaxf(M, ml_s[t][tid]);
+        float den = 0.f;
+        for (int t = 0; t < S; ++t) {
+          const float mt = ml_s[t][tid];
+          const float wgt = mt == -INFINITY ? 0.f : exp2f(mt - M);
+          ml_s[t][tid] = wgt;                       // weight of split t for head tid
+          den += wgt * ml_s[t][G + tid];
+        }
+        w_s[tid] = vscale / den;
+      }
+      __syncthreads();
+    }
 #pragma unroll
-    for (int t = 0; t < kMaxSplits; ++t)
-      vals[t] = t < S ? __hip_atomic_load(unit + (int64_t)t * pstride + idx, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT)
-                      : 0.f;
-    float num = 0.f;
+    for (int a = 0; a < kGroupOut; ++a) {
+      const int idx = base + a * blockDim.x + tid;
+      if (idx < nout) {
+        const int hh = idx / D;
+        float num = 0.f;
 #pragma unroll
-    for (int t = 0; t < kMaxSplits; ++t)
-      if (t < S) num += ml_s[t][hh] * vals[t];
-    const float val = num * w_s[hh];
-    const int64_t oi = ((int64_t)q * Hq + g * G) * D + idx;
-    if (kOutBf16) static_cast<__bf16*>(p.out)[oi] = (__bf16)val;
-    else static_cast<float*>(p.out)[oi] = val;
+        for (int t = 0; t < kMaxSplits; ++t)
+          if (t < S) num += ml_s[t][hh] * vals[a][t];
+        const float val = num * w_s[hh];
+        const int64_t oi = ((int64_t)q * Hq + g * G) * D + idx;
+        if (kOutBf16) static_cast<__bf16*>(p.out)[oi] = (__bf16)val;
+        else static_cast<float*>(p.out)[oi] = val;
+      }
+    }
   }
   if (tid == 0) p.counters[(q * Hkv + g) * kCounterStride] = 0u;
 }
@@ -375,7 +489,7 @@ hipError_t launch_attn(const Meta& m, const AttnArgs& a, hipStream_t stream) {
   p.sm_scale_log2 = a.sm_scale * 1.4426950408889634f;
   p.splits = sp.splits;
   p.cps = sp.chunks_per_split;
-  dim3 grid((unsigned)m.num_q, (unsigned)sp.splits, (unsigned)a.num_kv_heads);
+  const dim3 grid((unsigned)((int64_t)m.num_q * sp.splits * a.num_kv_heads));
   if (a.kv_fp8) {
     if (a.out_bf16) attn_kernel<true, true><<<grid, 256, 0, stream>>>(p);
     else attn_kernel<true, false><<<grid, 256, 0, stream>>>(p);

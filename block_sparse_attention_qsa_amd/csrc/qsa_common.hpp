@@ -102,7 +102,7 @@ struct AttnSplit {
 __host__ __device__ inline AttnSplit attn_split(int num_q, int num_kv_heads, int width) {
   const int chunks = (width + kChunk - 1) / kChunk;
   const int units = num_q * num_kv_heads;
-  const int target_wgs = 1024;
+  const int target_wgs = 512;    // two 4-wave workgroups per CU are resident at once
   int splits = (target_wgs + units - 1) / units;
   int max_splits = (chunks + kAttnWaves - 1) / kAttnWaves;   // <= kMaxSplits for width <= QSA_WIDTH
   if (splits > max_splits) splits = max_splits;

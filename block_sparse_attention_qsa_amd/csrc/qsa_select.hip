@@ -7,7 +7,9 @@
 // article (first optimisation) adds the last step: locate the kept pieces in
 // the KV cache.
 //
-// One 1024-thread workgroup handles one query:
+// One 1024-thread workgroup handles one query.  Rows of up to 65,536 blocks
+// are held in registers (contiguous segment per thread); longer rows use a
+// streaming variant that stages only the threshold bin's keys in LDS.
 //   1. FP32 scores -> order-preserving uint32 keys (-0.0 folded onto +0.0),
 //      staged in LDS when they fit.
 //   2. Three MSB-first radix passes (11, 11, 10 bits) with LDS histograms find
@@ -41,44 +43,181 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
   }
 }
 
-// One wave scans hist[2047 .. 0] from the top and finds the bin where the
-// running count first reaches krem; that lane stores the refined prefix and
-// the count still to take inside the bin and the bin's population.  Lane l
-// owns bins 2016-32l .. 2047-32l.
+// One wave finds, scanning hist[2047 .. 0] from the top, the bin where the
+// running count first reaches krem, and publishes the refined prefix, the
+// count still to take inside that bin and the bin's population.  Level one:
+// lane l sums bins 2016-32l .. 2047-32l and a wave scan picks the lane; level
+// two: lanes 0..31 take that lane's 32 bins (highest first) and a second scan
+// picks the bin.  No loops, no per-bin branches.
 __device__ __forceinline__ void find_bucket(const uint32_t* hist, uint32_t krem, uint32_t prefix, int shift,
                                             uint32_t* s_prefix, uint32_t* s_krem, uint32_t* s_count) {
-  const int lo = kRadixBins - 32 - 32 * lane_id();
-  uint32_t c[32];
+  const int lane = lane_id();
+  const int lo = kRadixBins - 32 - 32 * lane;
   const u32x4* h4 = reinterpret_cast<const u32x4*>(hist + lo);
+  uint32_t sum = 0;
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
     const u32x4 x = h4[v];
-    c[4 * v + 0] = x.x;
-    c[4 * v + 1] = x.y;
-    c[4 * v + 2] = x.z;
-    c[4 * v + 3] = x.w;
+    sum += x.x + x.y + x.z + x.w;
   }
-  uint32_t sum = 0;
-#pragma unroll
-  for (int b = 0; b < 32; ++b) sum += c[b];
   const uint32_t inc = wave_inclusive_scan(sum);
   const uint32_t exc = inc - sum;
-  if (exc < krem && krem <= inc) {
-    uint32_t run = exc;
-#pragma unroll
-    for (int b = 31; b >= 0; --b) {
-      if (run < krem && krem <= run + c[b]) {
-        *s_prefix = prefix | ((uint32_t)(lo + b) << shift);
-        *s_krem = krem - run;
-        *s_count = c[b];
-      }
-      run += c[b];
+  const uint64_t hit = __ballot(exc < krem && krem <= inc);
+  if (hit == 0) return;                                // unreachable while krem <= population
+  const int lh = __builtin_ctzll(hit);
+  const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)exc, lh);
+  const int lo_h = kRadixBins - 32 - 32 * lh;
+  const uint32_t cb = lane < 32 ? hist[lo_h + 31 - lane] : 0u;
+  const uint32_t run = above + wave_inclusive_scan(cb) - cb;
+  const uint64_t hit2 = __ballot(lane < 32 && run < krem && krem <= run + cb);
+  if (hit2 == 0) return;
+  if (lane == __builtin_ctzll(hit2)) {
+    *s_prefix = prefix | ((uint32_t)(lo_h + 31 - lane) << shift);
+    *s_krem = krem - run;
+    *s_count = cb;
+  }
+}
+
+// Register-resident selector for rows of at most E * 1024 keys: thread t
+// holds the contiguous keys [t*seg, t*seg + seg) (seg <= E, a multiple of 4)
+// in registers through the histogram passes and the ordered compaction.
+template <int E, bool kWritePos>
+__global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, const float* __restrict__ scores,
+                                                                    int64_t ld, int k, int32_t* __restrict__ sel,
+                                                                    int32_t* __restrict__ n_sel,
+                                                                    int32_t* __restrict__ pos,
+                                                                    int32_t* __restrict__ n_pos, int width) {
+  constexpr int NT = kSelectThreads;
+  __shared__ uint32_t hist[2][kRadixBins];
+  __shared__ uint32_t scan_scratch[NT / kWave];
+  __shared__ uint32_t s_prefix, s_krem, s_count;
+
+  const int q = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid / kWave;
+  const int r = request_of(m.q_start, m.num_req, q);
+  const int qs = m.q_start[r];
+  const int nq = m.q_start[r + 1] - qs;
+  const int L = m.seq_len[r] - nq + 1 + (q - qs);
+  int nf = L >> 2;
+  if (nf > m.max_blocks) nf = m.max_blocks;
+  if (nf > E * NT) nf = E * NT;                      // launcher picks E >= max_blocks / 1024
+  const int pl = L & 3;
+  const int kv0 = m.kv_start[r];
+  const float* srow = scores + (int64_t)q * ld;
+  int32_t* sel_row = sel + (int64_t)q * k;
+  int32_t* pos_row = kWritePos ? pos + (int64_t)q * width : nullptr;
+
+  if (nf <= k) {
+    for (int i = tid; i < k; i += NT) sel_row[i] = i < nf ? i : -1;
+    if (kWritePos) {
+      const int np = 4 * nf + pl;
+      for (int i = tid; i < width; i += NT) pos_row[i] = i < np ? kv0 + i : -1;
     }
+    if (tid == 0) {
+      n_sel[q] = nf;
+      if (kWritePos) n_pos[q] = 4 * nf + pl;
+    }
+    return;
+  }
+
+  // ---- keys of this thread's segment.  Slots past the row hold key 0: every
+  // finite score maps to a key >= 0x00800000 (top-11-bit digit >= 4), so with
+  // nf > k the zeros sit alone in the lowest bin and never reach the threshold.
+  const int seg = ((nf + NT - 1) / NT + 3) & ~3;
+  const int beg = min(tid * seg, nf);
+  const int cnt = min(seg, nf - beg);
+  const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
+  uint32_t kk[E];
+#pragma unroll
+  for (int v = 0; v < E / 4; ++v) {
+    const int e = 4 * v;
+    if (vec && e + 4 <= cnt) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(srow + beg + e);
+      kk[e] = score_key(x.x);
+      kk[e + 1] = score_key(x.y);
+      kk[e + 2] = score_key(x.z);
+      kk[e + 3] = score_key(x.w);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) kk[e + u] = e + u < cnt ? score_key(srow[beg + e + u]) : 0u;
+    }
+  }
+  for (int i = tid; i < 2 * kRadixBins; i += NT) (&hist[0][0])[i] = 0u;
+  __syncthreads();
+
+  // ---- MSB-first radix passes (11, 11, 10 bits); stop early once the
+  // threshold bin is taken whole.
+  uint32_t prefix = 0u, pmask = 0u, krem = (uint32_t)k;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+    uint32_t* cur = hist[pass & 1];
+    uint32_t* nxt = hist[(pass + 1) & 1];
+#pragma unroll
+    for (int e = 0; e < E; ++e) hist_add(cur, (kk[e] >> shift) & dmask, (kk[e] & pmask) == prefix);
+    for (int i = tid; i < kRadixBins; i += NT) nxt[i] = 0u;   // last read before the previous barrier
+    __syncthreads();
+    if (wave == 0) find_bucket(cur, krem, prefix, shift, &s_prefix, &s_krem, &s_count);
+    __syncthreads();
+    prefix = s_prefix;
+    krem = s_krem;
+    const uint32_t bin_count = s_count;
+    pmask |= dmask << shift;
+    if (krem == bin_count) break;
+  }
+  const uint32_t T = prefix, M = pmask, need = krem;
+
+  // ---- ordered compaction: keep (key & M) > T, and the first `need` keys with
+  // (key & M) == T in index order.  One packed scan: > T count in the high 12
+  // bits, == T count in the low 20.
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t km = kk[e] & M;
+    gt += km > T;
+    eq += km == T;
+  }
+  uint32_t tot;
+  const uint32_t before = block_exclusive_scan<NT>((gt << 20) | eq, scan_scratch, &tot);
+  const uint32_t eq_before = before & 0xFFFFFu;
+  uint32_t o = (before >> 20) + min(eq_before, need);
+  uint32_t seen = eq_before;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t km = kk[e] & M;
+    bool take = km > T;
+    if (km == T) {
+      take = seen < need;
+      ++seen;
+    }
+    if (take) {
+      const int i = beg + e;
+      sel_row[o] = i;
+      if (kWritePos) {
+        const int p0 = kv0 + 4 * i;
+        pos_row[4 * o + 0] = p0;
+        pos_row[4 * o + 1] = p0 + 1;
+        pos_row[4 * o + 2] = p0 + 2;
+        pos_row[4 * o + 3] = p0 + 3;
+      }
+      ++o;
+    }
+  }
+  if (kWritePos) {
+    for (int i = 4 * k + tid; i < width; i += NT) {
+      const int t = i - 4 * k;
+      pos_row[i] = t < pl ? kv0 + 4 * nf + t : -1;
+    }
+  }
+  if (tid == 0) {
+    n_sel[q] = k;
+    if (kWritePos) n_pos[q] = 4 * k + pl;
   }
 }
 
 template <bool kWritePos>
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(Meta m, const float* __restrict__ scores,
+__global__ __launch_bounds__(kSelectThreads) void select_stream_kernel(Meta m, const float* __restrict__ scores,
                                                                 int64_t ld, int k, int32_t* __restrict__ sel,
                                                                 int32_t* __restrict__ n_sel,
                                                                 int32_t* __restrict__ pos,
@@ -309,13 +448,26 @@ __global__ __launch_bounds__(256) void build_index_kernel(Meta m, const int32_t*
   if (threadIdx.x == 0) n_pos[q] = np;
 }
 
+template <bool kWritePos>
+static void launch_select_t(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel, int32_t* n_sel,
+                            int32_t* pos, int32_t* n_pos, int width, hipStream_t stream) {
+  const dim3 grid(m.num_q), block(kSelectThreads);
+  if (m.max_blocks <= 16 * kSelectThreads)
+    select_reg_kernel<16, kWritePos><<<grid, block, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
+  else if (m.max_blocks <= 32 * kSelectThreads)
+    select_reg_kernel<32, kWritePos><<<grid, block, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
+  else if (m.max_blocks <= 64 * kSelectThreads)
+    select_reg_kernel<64, kWritePos><<<grid, block, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
+  else
+    select_stream_kernel<kWritePos><<<grid, block, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
+}
+
 hipError_t launch_select(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel, int32_t* n_sel,
                          int32_t* pos, int32_t* n_pos, int width, hipStream_t stream) {
   if (pos)
-    select_kernel<true><<<m.num_q, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
+    launch_select_t<true>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, stream);
   else
-    select_kernel<false><<<m.num_q, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, n_sel, nullptr, nullptr,
-                                                                 width);
+    launch_select_t<false>(m, scores, ld, k, sel, n_sel, nullptr, nullptr, width, stream);
   return hipGetLastError();
 }
 

@@ -88,17 +88,27 @@ def _select_case(nfs, kind, seed):
     return rows
 
 
+SELECT_GROUPS = {
+    # one launch per group: the largest row decides which selector variant runs
+    "le16k": [0, 1, 511, 512, 513, 1000, 2048, 12500, 16383, 16384],
+    "le32k": [3, 513, 4097, 16385, 20000, 32768],
+    "le64k": [600, 32769, 40000, 65535, 65536],
+    "stream": [700, 12500, 65537, 100000, 131072],
+}
+
+
+@pytest.mark.parametrize("group", list(SELECT_GROUPS))
 @pytest.mark.parametrize("kind", ["ties", "normal", "zeros", "wide", "flat"])
-def test_select_bit_exact(kind):
+def test_select_bit_exact(kind, group):
     need_gpu()
-    nfs = [0, 1, 511, 512, 513, 1000, 2048, 12500, 16384, 16385, 40000, 65536]
-    rows = _select_case(nfs, kind, seed=301 + len(kind))
-    say("qsa_select_topk", kind, nfs)
+    nfs = SELECT_GROUPS[group]
+    rows = _select_case(nfs, kind, seed=301 + len(kind) + 7 * len(group))
+    say("qsa_select_topk", kind, group, nfs)
     B = len(nfs)
     seq = [4 * nf + (i % 4) for i, nf in enumerate(nfs)]
     seq = [max(s, 1) for s in seq]
     b = qsa.Batch(np.arange(B + 1), seq, np.zeros(B), np.zeros(B))
-    ld = b.max_blocks + 3
+    ld = b.max_blocks + (3 if kind in ("ties", "wide") else 0)    # unaligned rows too
     S = np.zeros((B, ld), np.float32)
     for i, s in enumerate(rows):
         S[i, :len(s)] = s
