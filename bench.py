@@ -180,19 +180,51 @@ def measure(name: str, steps: int, warmup: int, kernels: bool = True) -> dict:
     return res
 
 
-KERNEL_NAMES = {"score": "qsa::score_kernel", "select": "qsa::select_kernel", "attn": "qsa::attn_kernel"}
+KERNEL_NAMES = {"score": "qsa::score_kernel", "select": "qsa::select_reg_kernel", "attn": "qsa::attn_kernel"}
+CSRC = os.path.join(ROOT, "block_sparse_attention_qsa_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over every HIP source and header of the library (sorted by name)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    with open(os.path.join(ROOT, "include", "qsa.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
 
 
 def roofline_of(res: dict, traffic: dict | None) -> dict:
+    """Roofline of the dominant kernel.  `traffic` is HBM bytes per launch from
+    rocprofv3 FETCH_SIZE + WRITE_SIZE counters (each scaled by what the counter
+    reads for a 1 GiB device copy), taken only while the library's sources are
+    unchanged since the counters were collected."""
     ks = res["kernels"]
     dom = max(ks, key=lambda s: ks[s]["us"])
     k = ks[dom]
     tr = None
-    if traffic and traffic.get("kernel") == KERNEL_NAMES[dom] and traffic.get("workload") == res["workload"]:
-        tr = traffic.get("bytes_per_launch")
+    key = f"{KERNEL_NAMES[dom]}@{res['workload']}"
+    if traffic and key in traffic.get("entries", {}) and traffic.get("source_sha256") == kernel_source_hash():
+        tr = traffic["entries"][key]["bytes_per_launch"]
     return {"kernel": KERNEL_NAMES[dom], "bound": "hbm", "achieved": round(k["gbps"], 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(k["gbps"] / HBM_PEAK_GBPS, 4), "traffic": tr,
             "algorithmic_bytes_per_launch": k["bytes"], "avg_launch_us": round(k["us"], 3)}
+
+
+def calibrate_copy(gib: int = 1, reps: int = 3) -> None:
+    """A plain device-to-device copy of known size, for scaling memory counters."""
+    import torch
+    src = torch.empty(gib << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[calibrate] copied {gib} GiB x {reps}")
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 # ------------------------------------------------------------------ CPU baseline
@@ -230,6 +262,8 @@ def main():
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timings")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured by rocprofv3 counters")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a 1 GiB device copy (reference for memory-counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (run with --gpus 1)",
@@ -242,6 +276,8 @@ def main():
         sys.exit(1)
     import block_sparse_attention_qsa_amd as qsa
     qsa.lib()
+    if args.calibrate_copy:
+        calibrate_copy()
 
     res = measure(args.config, args.steps, args.warmup, kernels=not args.no_kernels)
     w = res.pop("w")
