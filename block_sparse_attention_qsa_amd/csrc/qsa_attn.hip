@@ -26,14 +26,28 @@
 // waves of a workgroup merge in LDS, and when a unit is split over several
 // workgroups the last one to finish merges the partials (an arrival counter
 // in the workspace, one 128-byte line per unit, reset to zero by that last
-// workgroup).  Partials travel through device-coherent stores and loads, so
-// the hand-off needs no cache flush or invalidation.
+// workgroup).  Partials travel through 16-byte device-scope stores and loads
+// that bypass the per-XCD caches, so the hand-off needs no cache flush or
+// invalidation.
 #include "qsa_common.hpp"
 #include "qsa_launch.hpp"
 
 namespace qsa {
 
 constexpr int kOStride = QSA_HEAD_DIM + 4;   // padded LDS row of one head's output
+// Device-scope (sc1) 16-byte loads and stores through a raw buffer descriptor
+// of a split-partial region: they bypass the per-XCD caches, so workgroups on
+// different XCDs see each other's partials without any cache flush.
+constexpr int kCpolSc1 = 16;                 // cache-policy bit SC1 (device scope)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ f32x4 load_coherent(__amdgpu_buffer_rsrc_t r, int float_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, float_off * 4, 0, kCpolSc1);
+}
+__device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, int float_off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, float_off * 4, 0, kCpolSc1);
+}
 constexpr int kMaxHeads = 8 * ((QSA_WIDTH + kChunk - 1) / kChunk);   // block heads of one split
 constexpr float kRescaleSlack = 8.f;     // log2 headroom of the softmax reference maximum
 
@@ -360,45 +374,46 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
     return;
   }
 
-  // Split partial: [G*128 unnormalised O][16 m][16 l] per (q, g, s), published
-  // with device-coherent (write-through) stores: no cache flush is needed
-  // before the arrival is counted, only the stores' completion.
+  // Split partial: [G*128 unnormalised O][16 m][16 l] floats per (q, g, s),
+  // written with 16-byte device-scope stores (they bypass the per-XCD caches),
+  // so no cache flush is needed before the arrival is counted; only the
+  // stores' completion.
   const int pstride = G * D + 32;
   float* unit = p.part + ((int64_t)q * Hkv + g) * p.splits * pstride;
-  float* mine = unit + (int64_t)s * pstride;
-  for (int idx = tid; idx < nout + 2 * G; idx += blockDim.x) {
-    float val;
-    int dst;
-    if (idx < nout) {
-      const int hh = idx / D, d = idx % D;
+  const __amdgpu_buffer_rsrc_t unit_rs = partial_rsrc(unit);
+  const int mine = s * pstride;
+  for (int v4 = tid; v4 < (nout + 32) / 4; v4 += blockDim.x) {
+    f32x4 val;
+    if (4 * v4 < nout) {
+      const int hh = (4 * v4) / D, d = (4 * v4) % D;
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, m_s[w][hh]);
-      float num = 0.f;
+      val = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w)
-        num += (m_s[w][hh] == -INFINITY ? 0.f : exp2f(m_s[w][hh] - M)) * o_s[w][hh][d];
-      val = num;
-      dst = idx;
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const float sc = m_s[w][hh] == -INFINITY ? 0.f : exp2f(m_s[w][hh] - M);
+        val += sc * *reinterpret_cast<const f32x4*>(&o_s[w][hh][d]);
+      }
     } else {
-      const int hh = (idx - nout) % G;
-      const bool is_l = (idx - nout) >= G;
-      float M = -INFINITY;
+      // m (heads 0..15) then l (heads 0..15), 4 heads per vector
+      const int r4 = 4 * v4 - nout;
+      const bool is_l = r4 >= 16;
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, m_s[w][hh]);
-      if (!is_l) {
-        val = M;
-        dst = nout + hh;
-      } else {
-        float den = 0.f;
+      for (int c = 0; c < 4; ++c) {
+        const int hh = (r4 & 15) + c;
+        float M = -INFINITY, den = 0.f;
+        if (hh < G) {
 #pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w)
-          den += (m_s[w][hh] == -INFINITY ? 0.f : exp2f(m_s[w][hh] - M)) * l_s[w][hh];
-        val = den;
-        dst = nout + 16 + hh;
+          for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, m_s[w][hh]);
+#pragma unroll
+          for (int w = 0; w < kAttnWaves; ++w)
+            den += (m_s[w][hh] == -INFINITY ? 0.f : exp2f(m_s[w][hh] - M)) * l_s[w][hh];
+        }
+        val[c] = is_l ? den : M;
       }
     }
-    __hip_atomic_store(mine + dst, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    store_coherent(unit_rs, mine + 4 * v4, val);
   }
   __builtin_amdgcn_s_waitcnt(0);     // this thread's stores have reached the coherence point
   __syncthreads();
@@ -409,26 +424,22 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   __syncthreads();
   if (!s_last) return;
 
-  // Last workgroup of the unit: merge all splits with device-coherent loads.
-  // The split maxima/sums and the first round of numerators are loaded together.
+  // Last workgroup of the unit: 16-byte device-scope loads bring every
+  // split's maxima, sums and numerators (one round for groups of <= 8 heads).
   const int S = p.splits;
-  float vals[kGroupOut][kMaxSplits];
-  for (int i = tid; i < S * 2 * G; i += blockDim.x) {
-    const int t = i / (2 * G), r = i % (2 * G);
-    const int off = r < G ? nout + r : nout + 16 + (r - G);
-    ml_s[t][r] = __hip_atomic_load(unit + (int64_t)t * pstride + off, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid < S * 8) {
+    const int t = tid / 8, r4 = tid % 8;
+    *reinterpret_cast<f32x4*>(&ml_s[t][4 * r4]) = load_coherent(unit_rs, t * pstride + nout + 4 * r4);
   }
-  for (int base = 0; base < nout; base += kGroupOut * blockDim.x) {
+  // Rounds of one 4-output vector per thread (one round for groups of <= 8 heads).
+  for (int v0 = 0; v0 < nout / 4; v0 += blockDim.x) {
+    const int v4 = v0 + tid;
+    f32x4 vals[kMaxSplits];
 #pragma unroll
-    for (int a = 0; a < kGroupOut; ++a) {
-      const int idx = base + a * blockDim.x + tid;
-#pragma unroll
-      for (int t = 0; t < kMaxSplits; ++t)
-        vals[a][t] = (t < S && idx < nout) ? __hip_atomic_load(unit + (int64_t)t * pstride + idx, __ATOMIC_RELAXED,
-                                                              __HIP_MEMORY_SCOPE_AGENT)
-                                           : 0.f;
-    }
-    if (base == 0) {
+    for (int t = 0; t < kMaxSplits; ++t)
+      vals[t] = (t < S && v4 < nout / 4) ? load_coherent(unit_rs, t * pstride + 4 * v4)
+                                         : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (v0 == 0) {
       __syncthreads();
       if (tid < G) {
         float M = -INFINITY;
@@ -438,25 +449,28 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
           const float mt = ml_s[t][tid];
           const float wgt = mt == -INFINITY ? 0.f : exp2f(mt - M);
           ml_s[t][tid] = wgt;                       // weight of split t for head tid
-          den += wgt * ml_s[t][G + tid];
+          den += wgt * ml_s[t][16 + tid];
         }
         w_s[tid] = vscale / den;
       }
       __syncthreads();
     }
+    if (v4 < nout / 4) {
+      const int hh = (4 * v4) / D;
+      f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int a = 0; a < kGroupOut; ++a) {
-      const int idx = base + a * blockDim.x + tid;
-      if (idx < nout) {
-        const int hh = idx / D;
-        float num = 0.f;
-#pragma unroll
-        for (int t = 0; t < kMaxSplits; ++t)
-          if (t < S) num += ml_s[t][hh] * vals[a][t];
-        const float val = num * w_s[hh];
-        const int64_t oi = ((int64_t)q * Hq + g * G) * D + idx;
-        if (kOutBf16) static_cast<__bf16*>(p.out)[oi] = (__bf16)val;
-        else static_cast<float*>(p.out)[oi] = val;
+      for (int t = 0; t < kMaxSplits; ++t)
+        if (t < S) num += ml_s[t][hh] * vals[t];
+      num *= w_s[hh];
+      const int64_t oi = ((int64_t)q * Hq + g * G) * D + 4 * v4;
+      if (kOutBf16) {
+        __bf16* op = static_cast<__bf16*>(p.out) + oi;
+        op[0] = (__bf16)num.x;
+        op[1] = (__bf16)num.y;
+        op[2] = (__bf16)num.z;
+        op[3] = (__bf16)num.w;
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + oi) = num;
       }
     }
   }

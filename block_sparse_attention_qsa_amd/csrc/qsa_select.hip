@@ -79,8 +79,8 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, uint32_t krem,
 }
 
 // Register-resident selector for rows of at most E * 1024 keys: thread t
-// holds the contiguous keys [t*seg, t*seg + seg) (seg <= E, a multiple of 4)
-// in registers through the histogram passes and the ordered compaction.
+// holds the contiguous keys [t*E, t*E + E) in registers through the histogram
+// passes and the ordered compaction.
 template <int E, bool kWritePos>
 __global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, const float* __restrict__ scores,
                                                                     int64_t ld, int k, int32_t* __restrict__ sel,
@@ -94,6 +94,29 @@ __global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, cons
 
   const int q = blockIdx.x;
   const int tid = threadIdx.x, wave = tid / kWave;
+  const float* srow = scores + (int64_t)q * ld;
+
+  // Score loads are issued first, speculatively: thread t owns the fixed segment
+  // [t*E, t*E + E) clipped to the row stride, so the loads do not wait for the
+  // request metadata; keys past the query's block count are zeroed afterwards.
+  const int beg = tid * E;
+  const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
+  float sv[E];
+#pragma unroll
+  for (int v = 0; v < E / 4; ++v) {
+    const int i = beg + 4 * v;
+    if (vec && i + 4 <= ld) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(srow + i);
+      sv[4 * v] = x.x;
+      sv[4 * v + 1] = x.y;
+      sv[4 * v + 2] = x.z;
+      sv[4 * v + 3] = x.w;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sv[4 * v + u] = i + u < ld ? srow[i + u] : 0.f;
+    }
+  }
+
   const int r = request_of(m.q_start, m.num_req, q);
   const int qs = m.q_start[r];
   const int nq = m.q_start[r + 1] - qs;
@@ -103,7 +126,6 @@ __global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, cons
   if (nf > E * NT) nf = E * NT;                      // launcher picks E >= max_blocks / 1024
   const int pl = L & 3;
   const int kv0 = m.kv_start[r];
-  const float* srow = scores + (int64_t)q * ld;
   int32_t* sel_row = sel + (int64_t)q * k;
   int32_t* pos_row = kWritePos ? pos + (int64_t)q * width : nullptr;
 
@@ -123,25 +145,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, cons
   // ---- keys of this thread's segment.  Slots past the row hold key 0: every
   // finite score maps to a key >= 0x00800000 (top-11-bit digit >= 4), so with
   // nf > k the zeros sit alone in the lowest bin and never reach the threshold.
-  const int seg = ((nf + NT - 1) / NT + 3) & ~3;
-  const int beg = min(tid * seg, nf);
-  const int cnt = min(seg, nf - beg);
-  const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
+  const int cnt = max(0, min(E, nf - beg));
   uint32_t kk[E];
 #pragma unroll
-  for (int v = 0; v < E / 4; ++v) {
-    const int e = 4 * v;
-    if (vec && e + 4 <= cnt) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(srow + beg + e);
-      kk[e] = score_key(x.x);
-      kk[e + 1] = score_key(x.y);
-      kk[e + 2] = score_key(x.z);
-      kk[e + 3] = score_key(x.w);
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) kk[e + u] = e + u < cnt ? score_key(srow[beg + e + u]) : 0u;
-    }
-  }
+  for (int e = 0; e < E; ++e) kk[e] = e < cnt ? score_key(sv[e]) : 0u;
   for (int i = tid; i < 2 * kRadixBins; i += NT) (&hist[0][0])[i] = 0u;
   __syncthreads();
 
