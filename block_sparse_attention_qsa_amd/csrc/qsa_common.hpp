@@ -34,12 +34,18 @@ __device__ __forceinline__ int request_of(const int32_t* __restrict__ q_start, i
   return lo;
 }
 
-// Order-preserving map FP32 -> uint32 (larger float -> larger key); -0.0 maps
-// like +0.0 so that the two compare equal.
+// Order-preserving map FP32 -> uint32 (larger float -> larger key).  Adding
+// +0.0 turns -0.0 into +0.0 so that the two compare equal; NaN keeps its sign
+// and sorts beyond the infinities.
 __device__ __forceinline__ uint32_t score_key(float s) {
-  uint32_t u = __float_as_uint(s);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(s + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
+// Inverse of score_key (-0.0 comes back as +0.0; key 0 comes back as NaN).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  const uint32_t flip = (uint32_t)((int32_t)~key >> 31) | 0x80000000u;
+  return __uint_as_float(key ^ flip);
 }
 
 // DPP sum over the 16 lanes of a row; every lane of the row gets the total.
@@ -49,6 +55,39 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
   v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
   return v;
+}
+
+// A copy of a wave-uniform value that the compiler cannot prove equal to the
+// original: values derived from it are recomputed instead of being kept live
+// across phases (which would cost a register per element).
+template <class T>
+__device__ __forceinline__ T fresh_uniform(T x) {
+  static_assert(sizeof(T) == 4, "32-bit values only");
+  int v = __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, x));
+  asm volatile("" : "+s"(v));
+  return __builtin_bit_cast(T, v);
+}
+
+
+// Wave-wide maximum / minimum (all 64 lanes active); the result is uniform.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return max(a, b);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+  v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+  const uint32_t a = min((uint32_t)__builtin_amdgcn_readlane((int)v, 0), (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+  const uint32_t b = min((uint32_t)__builtin_amdgcn_readlane((int)v, 32), (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+  return min(a, b);
 }
 
 __device__ __forceinline__ float fdot2_bf16(uint32_t a, uint32_t b, float c) {
@@ -71,26 +110,35 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
   return v + (row > 0 ? r0 : 0u) + (row > 1 ? r1 : 0u) + (row > 2 ? r2 : 0u);
 }
 
-// Block-wide exclusive prefix sum for blockDim.x == NT (multiple of 64).
-// `scratch` needs NT/64 words of LDS.  Returns this thread's exclusive prefix
-// and the block total.  One barrier inside; the caller must separate two
-// calls that share `scratch` by a barrier.
+// Block-wide exclusive prefix sum for blockDim.x == NT (multiple of 64,
+// at most 4096).  `scratch` needs NT/64 words of LDS.  Returns this thread's
+// exclusive prefix and the block total.  One barrier inside; the caller must
+// separate two calls that share `scratch` by a barrier.  The wave totals are
+// combined by a second wave scan over lanes 0..NT/64-1 (no per-thread loop
+// over them, which would hold NT/64 registers).
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
   constexpr int NW = NT / kWave;
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  static_assert(NW <= kWave, "one wave combines the wave totals");
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
   const uint32_t inc = wave_inclusive_scan(v);
   if (lane == kWave - 1) scratch[wave] = inc;
   __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint32_t t = scratch[w];
-    before += w < wave ? t : 0u;
-    all += t;
-  }
-  *total = all;
+  const uint32_t t = lane < NW ? scratch[lane] : 0u;
+  const uint32_t tinc = wave_inclusive_scan(t);
+  *total = (uint32_t)__builtin_amdgcn_readlane((int)tinc, NW - 1);
+  const uint32_t before = wave > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)tinc, wave - 1) : 0u;
   return before + inc - v;
+}
+
+// Combine per-wave values that waves 0..nw-1 published in slots[0..nw-1]
+// (nw <= 64): lane l reads slot l and a wave reduction finishes; uniform.
+__device__ __forceinline__ uint32_t lds_slots_max(const uint32_t* slots, int nw) {
+  return wave_max_u32(lane_id() < nw ? slots[lane_id()] : 0u);
+}
+__device__ __forceinline__ uint32_t lds_slots_min(const uint32_t* slots, int nw) {
+  return wave_min_u32(lane_id() < nw ? slots[lane_id()] : 0xFFFFFFFFu);
 }
 
 // Attention split geometry shared by the launcher and the workspace sizing.

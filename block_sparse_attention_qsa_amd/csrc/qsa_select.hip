@@ -28,6 +28,14 @@ namespace qsa {
 
 constexpr int kKeyCap = 32768;   // keys staged in LDS (128 KiB of the 160 KiB a workgroup may use)
 constexpr int kBatch = 8;        // loads a thread keeps in flight while streaming scores
+constexpr int kCandCap = 256;    // threshold-bin population ranked directly
+
+// Inside the fully unrolled per-element loops: a scheduling fence every 8
+// elements, so the compiler does not compute all E derived values before
+// consuming them (with 64 keys per thread in registers that spills).
+__device__ __forceinline__ void sched_fence(int e) {
+  if ((e & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+}
 
 // Histogram increment for a wave: when every active lane carries the same
 // bin (long runs of tied scores) one lane adds the whole count.
@@ -78,9 +86,62 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, uint32_t krem,
   }
 }
 
-// Register-resident selector for rows of at most E * 1024 keys: thread t
-// holds the contiguous keys [t*E, t*E + E) in registers through the histogram
-// passes and the ordered compaction.
+// Per-thread bit set over the E elements of a segment (bit e = element e).
+template <int E>
+struct ElemBits {
+  static constexpr int W = (E + 31) / 32;
+  uint32_t w[W];
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int i = 0; i < W; ++i) w[i] = 0u;
+  }
+  // elements pushed from E-1 down to 0 land at their own bit
+  __device__ __forceinline__ void push(int e, bool b) { w[e >> 5] = w[e >> 5] + w[e >> 5] + (uint32_t)b; }
+  __device__ __forceinline__ void set(int e, bool b) { w[e >> 5] |= (uint32_t)b << (e & 31); }
+  __device__ __forceinline__ bool test(int e) const { return (w[e >> 5] >> (e & 31)) & 1u; }
+  __device__ __forceinline__ uint32_t count() const {
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < W; ++i) c += __popc(w[i]);
+    return c;
+  }
+};
+
+// Grid bin of a score: trunc(clamp((x - lo) * inv, -1, 2047)).  x - lo is
+// exact-or-rounded and never negative for x >= lo, the product and the clamp
+// and truncation are monotone, so a larger score never lands in a lower bin
+// and every score of the row gets a bin in [0, 2047]; -inf (empty slots)
+// gets -1.
+__device__ __forceinline__ int grid_bin(float x, float lo, float inv) {
+  float t = (x - lo) * inv;
+  t = fminf(fmaxf(t, -1.f), 2047.f);
+  return (int)t;
+}
+
+// Register-resident selector for rows of at most E * 1024 blocks.  Thread t
+// owns the contiguous segment [t*E, t*E + E): its scores stay in registers
+// (the upper half of a 64-wide segment in LDS) from the load to the end.
+//   1. One block reduction gives the row's smallest and largest score.  When
+//      both are finite and differ, one histogram pass bins the scores on a
+//      linear grid of 2,048 bins spanning [min, max] (grid_bin is monotone,
+//      so the bins partition the row in score order).  On dot-product scores
+//      the grid spreads the row evenly, the histogram atomics barely collide
+//      and the bin B0 holding the k-th best score is small.
+//   2. Each thread classifies its elements once into two bit sets: above B0
+//      (kept) and inside B0 (candidates).  Without a finite range every
+//      element is a candidate.
+//   3. The candidates decide the rest: kept whole when B0 fits; otherwise,
+//      when there are at most kCandCap of them, each one's exact rank (score
+//      descending, index ascending) is counted from an LDS copy; if they all
+//      tie the tie value is known; failing both, MSB-first radix passes over
+//      11, 11 and 10 key bits find the threshold key.  Candidates above the
+//      threshold join the kept set; those equal to it are tie candidates.
+//   4. One packed block scan of (kept, tie) counts places each thread's kept
+//      blocks in index order; tie blocks go to the lowest indices first.  The
+//      kept indices are staged in LDS and leave as coalesced rows of sel and
+//      pos.
+// Only the few candidate elements take the per-element branches of step 3;
+// the per-element work of the common path is a key, a bin and two compares.
 template <int E, bool kWritePos>
 __global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, const float* __restrict__ scores,
                                                                     int64_t ld, int k, int32_t* __restrict__ sel,
@@ -88,34 +149,50 @@ __global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, cons
                                                                     int32_t* __restrict__ pos,
                                                                     int32_t* __restrict__ n_pos, int width) {
   constexpr int NT = kSelectThreads;
+  constexpr int NW = NT / kWave;
+  constexpr int ER = E > 32 ? 32 : E;    // scores per thread held in registers
+  constexpr int EL = E - ER;             // the rest sit in LDS, column-major
+  __shared__ float slab[EL > 0 ? EL * NT : 1];
   __shared__ uint32_t hist[2][kRadixBins];
-  __shared__ uint32_t scan_scratch[NT / kWave];
-  __shared__ uint32_t s_prefix, s_krem, s_count;
+  __shared__ uint32_t red_s[2 * NW];    // per-wave key range of the row
+  __shared__ uint32_t red2_s[2 * NW];   // per-wave key range of the candidates
+  __shared__ uint32_t scan_s[NW];
+  __shared__ u32x2 cand_s[kCandCap];
+  __shared__ int32_t sel_s[QSA_TOPK];
+  __shared__ uint32_t s_prefix, s_krem, s_count, s_ncand, s_T, s_need;
 
   const int q = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid / kWave;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const float* srow = scores + (int64_t)q * ld;
 
   // Score loads are issued first, speculatively: thread t owns the fixed segment
-  // [t*E, t*E + E) clipped to the row stride, so the loads do not wait for the
-  // request metadata; keys past the query's block count are zeroed afterwards.
+  // [t*E, t*E + E), so the loads do not wait for the request metadata.  They
+  // go through a buffer descriptor bounded by the row stride, so reads past it
+  // return 0 without a branch and every load of a thread is in flight at once
+  // (slots past the query's block count are discarded afterwards).  With a
+  // stride that is a multiple of 4 a 16-byte group never straddles the bound.
   const int beg = tid * E;
-  const bool vec = (reinterpret_cast<uintptr_t>(srow) & 15) == 0;
+  const uint32_t row_bytes = (uint32_t)min(ld, (int64_t)(1 << 28)) * 4u;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(srow), 0, (int)row_bytes, 0x00020000);
   float sv[E];
+  if ((ld & 3) == 0) {
 #pragma unroll
-  for (int v = 0; v < E / 4; ++v) {
-    const int i = beg + 4 * v;
-    if (vec && i + 4 <= ld) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(srow + i);
+    for (int v = 0; v < E / 4; ++v) {
+      const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (beg + 4 * v) * 4, 0, 0));
       sv[4 * v] = x.x;
       sv[4 * v + 1] = x.y;
       sv[4 * v + 2] = x.z;
       sv[4 * v + 3] = x.w;
-    } else {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) sv[4 * v + u] = i + u < ld ? srow[i + u] : 0.f;
     }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      sv[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (beg + e) * 4, 0, 0));
   }
+  // LDS set-up overlaps the loads
+  for (int i = tid; i < kRadixBins; i += NT) hist[0][i] = 0u;
+  if (tid == 0) s_ncand = 0u;
 
   const int r = request_of(m.q_start, m.num_req, q);
   const int qs = m.q_start[r];
@@ -142,86 +219,266 @@ __global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, cons
     return;
   }
 
-  // ---- keys of this thread's segment.  Slots past the row hold key 0: every
-  // finite score maps to a key >= 0x00800000 (top-11-bit digit >= 4), so with
-  // nf > k the zeros sit alone in the lowest bin and never reach the threshold.
   const int cnt = max(0, min(E, nf - beg));
-  uint32_t kk[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) kk[e] = e < cnt ? score_key(sv[e]) : 0u;
-  for (int i = tid; i < 2 * kRadixBins; i += NT) (&hist[0][0])[i] = 0u;
-  __syncthreads();
+  const bool wave_full = __ballot(cnt != E) == 0;    // every lane holds E blocks
+  const bool wave_empty = __ballot(cnt != 0) == 0;   // no lane holds a block
 
-  // ---- MSB-first radix passes (11, 11, 10 bits); stop early once the
-  // threshold bin is taken whole.
-  uint32_t prefix = 0u, pmask = 0u, krem = (uint32_t)k;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
-    uint32_t* cur = hist[pass & 1];
-    uint32_t* nxt = hist[(pass + 1) & 1];
-#pragma unroll
-    for (int e = 0; e < E; ++e) hist_add(cur, (kk[e] >> shift) & dmask, (kk[e] & pmask) == prefix);
-    for (int i = tid; i < kRadixBins; i += NT) nxt[i] = 0u;   // last read before the previous barrier
-    __syncthreads();
-    if (wave == 0) find_bucket(cur, krem, prefix, shift, &s_prefix, &s_krem, &s_count);
-    __syncthreads();
-    prefix = s_prefix;
-    krem = s_krem;
-    const uint32_t bin_count = s_count;
-    pmask |= dmask << shift;
-    if (krem == bin_count) break;
-  }
-  const uint32_t T = prefix, M = pmask, need = krem;
-
-  // ---- ordered compaction: keep (key & M) > T, and the first `need` keys with
-  // (key & M) == T in index order.  One packed scan: > T count in the high 12
-  // bits, == T count in the low 20.
-  uint32_t gt = 0, eq = 0;
+  // Slots past the row become -inf: below every score, grid bin -1.
+  float xr[ER];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const uint32_t km = kk[e] & M;
-    gt += km > T;
-    eq += km == T;
+    const float x = e < cnt ? sv[e] : -__builtin_inff();
+    if (e < ER) xr[e < ER ? e : 0] = x;
+    else slab[(e - ER) * NT + tid] = x;   // read back only by this thread
   }
-  uint32_t tot;
-  const uint32_t before = block_exclusive_scan<NT>((gt << 20) | eq, scan_scratch, &tot);
-  const uint32_t eq_before = before & 0xFFFFFu;
-  uint32_t o = (before >> 20) + min(eq_before, need);
-  uint32_t seen = eq_before;
+// score e of this thread's segment (e is a compile-time constant in the unrolled loops)
+#define QSA_X(e) ((e) < ER ? xr[(e) < ER ? (e) : 0] : slab[((e) - ER) * NT + tid])
+
+  // ---- 1. key range of the row (empty slots excluded)
+  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+  if (wave_full) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const uint32_t km = kk[e] & M;
-    bool take = km > T;
-    if (km == T) {
-      take = seen < need;
-      ++seen;
+    for (int e = 0; e < E; ++e) {
+      const uint32_t key = score_key(QSA_X(e));
+      kmax = max(kmax, key);
+      kmin = min(kmin, key);
     }
-    if (take) {
-      const int i = beg + e;
-      sel_row[o] = i;
-      if (kWritePos) {
-        const int p0 = kv0 + 4 * i;
-        pos_row[4 * o + 0] = p0;
-        pos_row[4 * o + 1] = p0 + 1;
-        pos_row[4 * o + 2] = p0 + 2;
-        pos_row[4 * o + 3] = p0 + 3;
+  } else if (!wave_empty) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t key = score_key(QSA_X(e));
+      kmax = max(kmax, key);                        // -inf never raises the maximum
+      kmin = min(kmin, e < cnt ? key : 0xFFFFFFFFu);
+    }
+  }
+  kmax = wave_max_u32(kmax);
+  kmin = wave_min_u32(kmin);
+  if (lane == 0) {
+    red_s[wave] = kmax;
+    red_s[NW + wave] = kmin;
+  }
+  __syncthreads();
+  kmax = lds_slots_max(red_s, NW);
+  kmin = lds_slots_min(red_s + NW, NW);
+  const float lo = key_value(kmin), hi = key_value(kmax);
+  const float span = hi - lo;
+  const float inv = (float)kRadixBins / span;
+  const bool grid =
+      __builtin_isfinite(lo) && __builtin_isfinite(hi) && span > 0.f && __builtin_isfinite(inv) && inv > 0.f;
+
+  // ---- 2. grid histogram and classification
+  int B0 = 0;
+  uint32_t krem = (uint32_t)k, c0 = (uint32_t)nf;
+  ElemBits<E> above, inb;
+  above.clear();
+  inb.clear();
+  if (grid) {
+    {
+      const float lo0 = fresh_uniform(lo), inv0 = fresh_uniform(inv);
+      if (wave_full) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          atomicAdd(&hist[0][grid_bin(QSA_X(e), lo0, inv0)], 1u);
+          sched_fence(e);
+        }
+      } else if (!wave_empty) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int b = grid_bin(QSA_X(e), lo0, inv0);
+          if (b >= 0) atomicAdd(&hist[0][b], 1u);
+          sched_fence(e);
+        }
       }
+    }
+    for (int i = tid; i < kRadixBins; i += NT) hist[1][i] = 0u;
+    __syncthreads();
+    if (wave == 0) find_bucket(hist[0], krem, 0u, 0, &s_prefix, &s_krem, &s_count);
+    __syncthreads();
+    B0 = fresh_uniform((int)s_prefix);
+    krem = fresh_uniform(s_krem);
+    c0 = fresh_uniform(s_count);
+    if (!wave_empty) {
+      const float lo1 = fresh_uniform(lo), inv1 = fresh_uniform(inv);
+#pragma unroll
+      for (int e = E - 1; e >= 0; --e) {
+        const int b = grid_bin(QSA_X(e), lo1, inv1);
+        above.push(e, b > B0);
+        inb.push(e, b == B0);
+        sched_fence(e);
+      }
+    }
+  } else {
+    // no finite range: every block of the row is a candidate
+#pragma unroll
+    for (int e = E - 1; e >= 0; --e) inb.push(e, e < cnt);
+  }
+
+  // ---- 3. resolve the candidates
+  ElemBits<E> keep = above, ties;
+  ties.clear();
+  uint32_t need = 0u;
+  if (grid && krem == c0) {
+#pragma unroll
+    for (int i = 0; i < ElemBits<E>::W; ++i) keep.w[i] |= inb.w[i];   // B0 kept whole
+  } else {
+    uint32_t T = 0u, M = 0xFFFFFFFFu;
+    bool done = false;
+    if (c0 <= (uint32_t)kCandCap) {
+      // stage the candidates (wave-aggregated append), then rank them
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const bool mine = inb.test(e);
+        const uint64_t bal = __ballot(mine);
+        if (bal) {
+          uint32_t wbase = 0;
+          if (lane == __builtin_ctzll(bal)) wbase = atomicAdd(&s_ncand, (uint32_t)__popcll(bal));
+          wbase = (uint32_t)__builtin_amdgcn_readlane((int)wbase, __builtin_ctzll(bal));
+          const uint32_t slot =
+              __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+          if (mine && wbase + slot < (uint32_t)kCandCap)
+            cand_s[wbase + slot] = u32x2{score_key(QSA_X(e)), (uint32_t)(beg + e)};
+        }
+      }
+      __syncthreads();
+      if (tid < (int)c0) {
+        const u32x2 me = cand_s[tid];
+        uint32_t higher = 0u, ahead = 0u;
+        for (int j = 0; j < (int)c0; ++j) {
+          const u32x2 o = cand_s[j];
+          higher += o.x > me.x;
+          ahead += (o.x == me.x) & (o.y < me.y);
+        }
+        if (higher + ahead == krem - 1u) {
+          s_T = me.x;
+          s_need = krem - higher;
+        }
+      }
+      __syncthreads();
+      T = s_T;
+      need = s_need;
+      done = true;
+    } else {
+      // many candidates: done at once if they all tie
+      uint32_t bmax = 0u, bmin = 0xFFFFFFFFu;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        if (inb.test(e)) {
+          const uint32_t key = score_key(QSA_X(e));
+          bmax = max(bmax, key);
+          bmin = min(bmin, key);
+        }
+      }
+      bmax = wave_max_u32(bmax);
+      bmin = wave_min_u32(bmin);
+      if (lane == 0) {
+        red2_s[wave] = bmax;
+        red2_s[NW + wave] = bmin;
+      }
+      __syncthreads();
+      bmax = lds_slots_max(red2_s, NW);
+      bmin = lds_slots_min(red2_s + NW, NW);
+      if (bmax == bmin) {
+        T = bmax;
+        need = krem;
+        done = true;
+      }
+    }
+    if (!done) {
+      // MSB-first radix passes (11, 11, 10 key bits) over the candidates;
+      // stop once the threshold bin is taken whole
+      uint32_t prefix = 0u, pmask = 0u;
+      int h = grid ? 1 : 0;
+#pragma unroll 1
+      for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
+        uint32_t* cur = hist[h];
+        uint32_t* nxt = hist[h ^ 1];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint32_t key = score_key(QSA_X(e));
+          hist_add(cur, (key >> shift) & dmask, inb.test(e) && (key & pmask) == prefix);
+          sched_fence(e);
+        }
+        for (int i = tid; i < kRadixBins; i += NT) nxt[i] = 0u;   // last read before the previous barrier
+        __syncthreads();
+        if (wave == 0) find_bucket(cur, krem, prefix, shift, &s_prefix, &s_krem, &s_count);
+        __syncthreads();
+        prefix = s_prefix;
+        krem = s_krem;
+        const uint32_t bin_count = s_count;
+        pmask |= dmask << shift;
+        h ^= 1;
+        if (krem == bin_count) break;
+      }
+      T = prefix;
+      M = pmask;
+      need = krem;
+    }
+    // split the candidates around the threshold
+    T = fresh_uniform(T);
+    M = fresh_uniform(M);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (inb.test(e)) {
+        const uint32_t km = score_key(QSA_X(e)) & M;
+        keep.set(e, km > T);
+        ties.set(e, km == T);
+      }
+    }
+  }
+
+  // ---- 4. ordered compaction: one packed scan, kept count in the high 12
+  // bits and tie count in the low 20
+  need = fresh_uniform(need);
+  const uint32_t nkeep = keep.count(), ntie = ties.count();
+  uint32_t tot;
+  const uint32_t before = block_exclusive_scan<NT>((nkeep << 20) | ntie, scan_s, &tot);
+  const uint32_t tie_before = before & 0xFFFFFu;
+  // ties kept by earlier threads, and by this one (need - kept never wraps)
+  const uint32_t kept = min(tie_before, need);
+  uint32_t take = min(need - kept, ntie);
+#pragma unroll
+  for (int i = 0; i < ElemBits<E>::W; ++i) {
+    uint32_t t = ties.w[i];
+    while (take != 0u && t != 0u) {
+      const uint32_t low = t & (0u - t);
+      keep.w[i] |= low;
+      t ^= low;
+      --take;
+    }
+  }
+  uint32_t o = (before >> 20) + kept;
+#pragma unroll
+  for (int i = 0; i < ElemBits<E>::W; ++i) {
+    uint32_t t = keep.w[i];
+    while (t != 0u) {
+      const int e = 32 * i + __builtin_ctz(t);
+      t &= t - 1u;
+      if (o < (uint32_t)k) sel_s[o] = beg + e;
       ++o;
     }
   }
+  const int ns = (int)min((tot >> 20) + min(tot & 0xFFFFFu, need), (uint32_t)k);
+  __syncthreads();
+  // the clamp only guards the position buffer against a broken invariant: a
+  // kept index always lies in [0, nf)
+  for (int i = tid; i < k; i += NT) sel_row[i] = i < ns ? min(max(sel_s[i], 0), nf - 1) : -1;
   if (kWritePos) {
-    for (int i = 4 * k + tid; i < width; i += NT) {
-      const int t = i - 4 * k;
-      pos_row[i] = t < pl ? kv0 + 4 * nf + t : -1;
+    const int np = 4 * ns + pl;
+    for (int i = tid; i < width; i += NT) {
+      int v = -1;
+      if (i < 4 * ns) v = kv0 + 4 * min(max(sel_s[i >> 2], 0), nf - 1) + (i & 3);
+      else if (i < np) v = kv0 + 4 * nf + (i - 4 * ns);
+      pos_row[i] = v;
     }
   }
   if (tid == 0) {
-    n_sel[q] = k;
-    if (kWritePos) n_pos[q] = 4 * k + pl;
+    n_sel[q] = ns;
+    if (kWritePos) n_pos[q] = 4 * ns + pl;
   }
 }
+#undef QSA_X
 
 template <bool kWritePos>
 __global__ __launch_bounds__(kSelectThreads) void select_stream_kernel(Meta m, const float* __restrict__ scores,

@@ -77,6 +77,12 @@ def _select_case(nfs, kind, seed):
             s = rng.choice(np.array([-0.0, 0.0, 1.0, -1.0], np.float32), nf)
         elif kind == "wide":
             s = (rng.standard_normal(nf) * 10.0 ** rng.integers(-30, 30, nf)).astype(np.float32)
+        elif kind == "inf":
+            # infinite scores leave the row without a finite range: the
+            # selector falls back to radix passes over the raw keys
+            s = rng.standard_normal(nf).astype(np.float32)
+            s[rng.random(nf) < 0.01] = np.inf
+            s[rng.random(nf) < 0.01] = -np.inf
         elif kind == "flat":
             # 60% of the blocks share the top score: the chosen top-level radix
             # bin can exceed what the selector stages in LDS
@@ -98,7 +104,7 @@ SELECT_GROUPS = {
 
 
 @pytest.mark.parametrize("group", list(SELECT_GROUPS))
-@pytest.mark.parametrize("kind", ["ties", "normal", "zeros", "wide", "flat"])
+@pytest.mark.parametrize("kind", ["ties", "normal", "zeros", "wide", "flat", "inf"])
 def test_select_bit_exact(kind, group):
     need_gpu()
     nfs = SELECT_GROUPS[group]
