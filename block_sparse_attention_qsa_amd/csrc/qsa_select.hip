@@ -53,12 +53,14 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, uint32_t bin, bool acti
 
 // One wave finds, scanning hist[2047 .. 0] from the top, the bin where the
 // running count first reaches krem, and publishes the refined prefix, the
-// count still to take inside that bin and the bin's population.  Level one:
-// lane l sums bins 2016-32l .. 2047-32l and a wave scan picks the lane; level
-// two: lanes 0..31 take that lane's 32 bins (highest first) and a second scan
-// picks the bin.  No loops, no per-bin branches.
+// count still to take inside that bin and the bin's population (and, when
+// s_total is given, the histogram's total).  Level one: lane l sums bins
+// 2016-32l .. 2047-32l and a wave scan picks the lane; level two: lanes 0..31
+// take that lane's 32 bins (highest first) and a second scan picks the bin.
+// No loops, no per-bin branches.
 __device__ __forceinline__ void find_bucket(const uint32_t* hist, uint32_t krem, uint32_t prefix, int shift,
-                                            uint32_t* s_prefix, uint32_t* s_krem, uint32_t* s_count) {
+                                            uint32_t* s_prefix, uint32_t* s_krem, uint32_t* s_count,
+                                            uint32_t* s_total = nullptr) {
   const int lane = lane_id();
   const int lo = kRadixBins - 32 - 32 * lane;
   const u32x4* h4 = reinterpret_cast<const u32x4*>(hist + lo);
@@ -69,9 +71,10 @@ __device__ __forceinline__ void find_bucket(const uint32_t* hist, uint32_t krem,
     sum += x.x + x.y + x.z + x.w;
   }
   const uint32_t inc = wave_inclusive_scan(sum);
+  if (s_total && lane == kWave - 1) *s_total = inc;
   const uint32_t exc = inc - sum;
   const uint64_t hit = __ballot(exc < krem && krem <= inc);
-  if (hit == 0) return;                                // unreachable while krem <= population
+  if (hit == 0) return;                                // krem exceeds the population
   const int lh = __builtin_ctzll(hit);
   const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)exc, lh);
   const int lo_h = kRadixBins - 32 - 32 * lh;
@@ -108,19 +111,43 @@ struct ElemBits {
 };
 
 // Grid bin of a score: trunc(clamp((x - lo) * inv, -1, 2047)).  x - lo is
-// exact-or-rounded and never negative for x >= lo, the product and the clamp
-// and truncation are monotone, so a larger score never lands in a lower bin
-// and every score of the row gets a bin in [0, 2047]; -inf (empty slots)
-// gets -1.
+// never negative for x >= lo, and the product, the clamp and the truncation
+// are monotone, so a larger score never lands in a lower bin and every score
+// of the row gets a bin in [0, 2047]; NaN (empty slots) gets -1.
 __device__ __forceinline__ int grid_bin(float x, float lo, float inv) {
   float t = (x - lo) * inv;
   t = fminf(fmaxf(t, -1.f), 2047.f);
   return (int)t;
 }
 
-// Register-resident selector for rows of at most E * 1024 blocks.  Thread t
-// owns the contiguous segment [t*E, t*E + E): its scores stay in registers
-// (the upper half of a 64-wide segment in LDS) from the load to the end.
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  const float a = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16)));
+  const float b = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float wave_min_f32(float v) {
+  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fminf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  const float a = fminf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16)));
+  const float b = fminf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
+                        __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
+  return fminf(a, b);
+}
+
+// Register-resident selector for rows of at most E * NT blocks, NT threads
+// per query.  Thread t owns the contiguous segment [t*E, t*E + E): its
+// scores stay in registers (the upper half of a 64-wide segment in LDS) from
+// the load to the end.
 //   1. One block reduction gives the row's smallest and largest score.  When
 //      both are finite and differ, one histogram pass bins the scores on a
 //      linear grid of 2,048 bins spanning [min, max] (grid_bin is monotone,
@@ -128,38 +155,44 @@ __device__ __forceinline__ int grid_bin(float x, float lo, float inv) {
 //      the grid spreads the row evenly, the histogram atomics barely collide
 //      and the bin B0 holding the k-th best score is small.
 //   2. Each thread classifies its elements once into two bit sets: above B0
-//      (kept) and inside B0 (candidates).  Without a finite range every
-//      element is a candidate.
+//      (kept) and inside B0 (candidates).  Without a finite range (or with a
+//      NaN score, found by the histogram missing blocks) every element is a
+//      candidate.
 //   3. The candidates decide the rest: kept whole when B0 fits; otherwise,
-//      when there are at most kCandCap of them, each one's exact rank (score
-//      descending, index ascending) is counted from an LDS copy; if they all
-//      tie the tie value is known; failing both, MSB-first radix passes over
-//      11, 11 and 10 key bits find the threshold key.  Candidates above the
-//      threshold join the kept set; those equal to it are tie candidates.
+//      when there are at most kCandCap of them (staged in LDS during step 2),
+//      each one's exact rank (score descending, index ascending) is counted
+//      and the kept ones are marked in an LDS bitmap; if they all tie, the
+//      lowest indices are kept; failing both, MSB-first radix passes over 11,
+//      11 and 10 key bits find the threshold key.
 //   4. One packed block scan of (kept, tie) counts places each thread's kept
 //      blocks in index order; tie blocks go to the lowest indices first.  The
 //      kept indices are staged in LDS and leave as coalesced rows of sel and
 //      pos.
-// Only the few candidate elements take the per-element branches of step 3;
-// the per-element work of the common path is a key, a bin and two compares.
-template <int E, bool kWritePos>
-__global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, const float* __restrict__ scores,
-                                                                    int64_t ld, int k, int32_t* __restrict__ sel,
-                                                                    int32_t* __restrict__ n_sel,
-                                                                    int32_t* __restrict__ pos,
-                                                                    int32_t* __restrict__ n_pos, int width) {
-  constexpr int NT = kSelectThreads;
+// The per-element work of the common path is a bin, two compares and a
+// ballot; only the few candidates take branches.
+template <int E, int NT, bool kWritePos>
+__global__ __launch_bounds__(NT) void select_reg_kernel(Meta m, const float* __restrict__ scores, int64_t ld,
+                                                        int k, int32_t* __restrict__ sel,
+                                                        int32_t* __restrict__ n_sel, int32_t* __restrict__ pos,
+                                                        int32_t* __restrict__ n_pos, int width) {
   constexpr int NW = NT / kWave;
   constexpr int ER = E > 32 ? 32 : E;    // scores per thread held in registers
   constexpr int EL = E - ER;             // the rest sit in LDS, column-major
+  constexpr int kMapWords = E * NT / 32;
+  static_assert(E == 16 || E == 32 || E == 64, "segment widths");
+  // candidates are staged during classification, except for 64-wide segments
+  // whose register budget leaves no room for it (they stage in a loop of
+  // their own)
+  constexpr bool kFuseStage = E <= 32;
   __shared__ float slab[EL > 0 ? EL * NT : 1];
   __shared__ uint32_t hist[2][kRadixBins];
-  __shared__ uint32_t red_s[2 * NW];    // per-wave key range of the row
-  __shared__ uint32_t red2_s[2 * NW];   // per-wave key range of the candidates
+  __shared__ uint32_t keepmap[kMapWords];   // kept candidates, bit per block
+  __shared__ float red_s[2 * NW];           // per-wave score range of the row
+  __shared__ uint32_t red2_s[2 * NW];       // per-wave key range of the candidates
   __shared__ uint32_t scan_s[NW];
   __shared__ u32x2 cand_s[kCandCap];
   __shared__ int32_t sel_s[QSA_TOPK];
-  __shared__ uint32_t s_prefix, s_krem, s_count, s_ncand, s_T, s_need;
+  __shared__ uint32_t s_prefix, s_krem, s_count, s_total, s_ncand;
 
   const int q = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
@@ -192,6 +225,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, cons
   }
   // LDS set-up overlaps the loads
   for (int i = tid; i < kRadixBins; i += NT) hist[0][i] = 0u;
+  for (int i = tid; i < kMapWords; i += NT) keepmap[i] = 0u;
   if (tid == 0) s_ncand = 0u;
 
   const int r = request_of(m.q_start, m.num_req, q);
@@ -200,7 +234,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, cons
   const int L = m.seq_len[r] - nq + 1 + (q - qs);
   int nf = L >> 2;
   if (nf > m.max_blocks) nf = m.max_blocks;
-  if (nf > E * NT) nf = E * NT;                      // launcher picks E >= max_blocks / 1024
+  if (nf > E * NT) nf = E * NT;                      // launcher picks E * NT >= max_blocks
   const int pl = L & 3;
   const int kv0 = m.kv_start[r];
   int32_t* sel_row = sel + (int64_t)q * k;
@@ -223,94 +257,105 @@ __global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, cons
   const bool wave_full = __ballot(cnt != E) == 0;    // every lane holds E blocks
   const bool wave_empty = __ballot(cnt != 0) == 0;   // no lane holds a block
 
-  // Slots past the row become -inf: below every score, grid bin -1.
+  // Slots past the row become NaN: the range reduction skips them and their
+  // grid bin is -1.
   float xr[ER];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const float x = e < cnt ? sv[e] : -__builtin_inff();
+    const float x = e < cnt ? sv[e] : __builtin_nanf("");
     if (e < ER) xr[e < ER ? e : 0] = x;
     else slab[(e - ER) * NT + tid] = x;   // read back only by this thread
   }
 // score e of this thread's segment (e is a compile-time constant in the unrolled loops)
 #define QSA_X(e) ((e) < ER ? xr[(e) < ER ? (e) : 0] : slab[((e) - ER) * NT + tid])
 
-  // ---- 1. key range of the row (empty slots excluded)
-  uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
-  if (wave_full) {
+  // ---- 1. score range of the row (NaN skipped)
+  float vmax = -__builtin_inff(), vmin = __builtin_inff();
+  if (!wave_empty) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const uint32_t key = score_key(QSA_X(e));
-      kmax = max(kmax, key);
-      kmin = min(kmin, key);
-    }
-  } else if (!wave_empty) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const uint32_t key = score_key(QSA_X(e));
-      kmax = max(kmax, key);                        // -inf never raises the maximum
-      kmin = min(kmin, e < cnt ? key : 0xFFFFFFFFu);
+      vmax = fmaxf(vmax, QSA_X(e));
+      vmin = fminf(vmin, QSA_X(e));
     }
   }
-  kmax = wave_max_u32(kmax);
-  kmin = wave_min_u32(kmin);
+  vmax = wave_max_f32(vmax);
+  vmin = wave_min_f32(vmin);
   if (lane == 0) {
-    red_s[wave] = kmax;
-    red_s[NW + wave] = kmin;
+    red_s[wave] = vmax;
+    red_s[NW + wave] = vmin;
   }
   __syncthreads();
-  kmax = lds_slots_max(red_s, NW);
-  kmin = lds_slots_min(red_s + NW, NW);
-  const float lo = key_value(kmin), hi = key_value(kmax);
+  const float hi = wave_max_f32(lane < NW ? red_s[lane] : -__builtin_inff());
+  const float lo = wave_min_f32(lane < NW ? red_s[NW + lane] : __builtin_inff());
   const float span = hi - lo;
   const float inv = (float)kRadixBins / span;
-  const bool grid =
-      __builtin_isfinite(lo) && __builtin_isfinite(hi) && span > 0.f && __builtin_isfinite(inv) && inv > 0.f;
+  bool grid = __builtin_isfinite(lo) && __builtin_isfinite(hi) && span > 0.f && __builtin_isfinite(inv) && inv > 0.f;
 
-  // ---- 2. grid histogram and classification
-  int B0 = 0;
+  // ---- 2. grid histogram, then classification
+  int B0 = 0, h = 0;
   uint32_t krem = (uint32_t)k, c0 = (uint32_t)nf;
-  ElemBits<E> above, inb;
-  above.clear();
-  inb.clear();
   if (grid) {
-    {
-      const float lo0 = fresh_uniform(lo), inv0 = fresh_uniform(inv);
-      if (wave_full) {
+    const float lo0 = fresh_uniform(lo), inv0 = fresh_uniform(inv);
+    if (wave_full) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          atomicAdd(&hist[0][grid_bin(QSA_X(e), lo0, inv0)], 1u);
-          sched_fence(e);
-        }
-      } else if (!wave_empty) {
+      for (int e = 0; e < E; ++e) {
+        atomicAdd(&hist[0][grid_bin(QSA_X(e), lo0, inv0)], 1u);
+        sched_fence(e);
+      }
+    } else if (!wave_empty) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int b = grid_bin(QSA_X(e), lo0, inv0);
-          if (b >= 0) atomicAdd(&hist[0][b], 1u);
-          sched_fence(e);
-        }
+      for (int e = 0; e < E; ++e) {
+        const int b = grid_bin(QSA_X(e), lo0, inv0);
+        if (b >= 0) atomicAdd(&hist[0][b], 1u);
+        sched_fence(e);
       }
     }
     for (int i = tid; i < kRadixBins; i += NT) hist[1][i] = 0u;
     __syncthreads();
-    if (wave == 0) find_bucket(hist[0], krem, 0u, 0, &s_prefix, &s_krem, &s_count);
+    if (wave == 0) find_bucket(hist[0], krem, 0u, 0, &s_prefix, &s_krem, &s_count, &s_total);
     __syncthreads();
-    B0 = fresh_uniform((int)s_prefix);
-    krem = fresh_uniform(s_krem);
-    c0 = fresh_uniform(s_count);
+    h = 1;
+    if (fresh_uniform(s_total) == (uint32_t)nf) {
+      B0 = fresh_uniform((int)s_prefix);
+      krem = fresh_uniform(s_krem);
+      c0 = fresh_uniform(s_count);
+    } else {
+      grid = false;   // a NaN score missed the histogram: no grid
+    }
+  }
+  const bool ranked = grid && krem != c0 && c0 <= (uint32_t)kCandCap;
+  ElemBits<E> above, inb;
+  above.clear();
+  inb.clear();
+  if (grid) {
     if (!wave_empty) {
       const float lo1 = fresh_uniform(lo), inv1 = fresh_uniform(inv);
 #pragma unroll
       for (int e = E - 1; e >= 0; --e) {
-        const int b = grid_bin(QSA_X(e), lo1, inv1);
+        const float x = QSA_X(e);
+        const int b = grid_bin(x, lo1, inv1);
         above.push(e, b > B0);
         inb.push(e, b == B0);
+        if (kFuseStage && ranked) {
+          // stage the candidate (wave-aggregated append)
+          const bool mine = b == B0;
+          const uint64_t bal = __ballot(mine);
+          if (bal) {
+            uint32_t wbase = 0;
+            if (lane == __builtin_ctzll(bal)) wbase = atomicAdd(&s_ncand, (uint32_t)__popcll(bal));
+            wbase = (uint32_t)__builtin_amdgcn_readlane((int)wbase, __builtin_ctzll(bal));
+            const uint32_t slot =
+                __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (mine && wbase + slot < (uint32_t)kCandCap)
+              cand_s[wbase + slot] = u32x2{score_key(x), (uint32_t)(beg + e)};
+          }
+        }
         sched_fence(e);
       }
     }
   } else {
-    // no finite range: every block of the row is a candidate
 #pragma unroll
-    for (int e = E - 1; e >= 0; --e) inb.push(e, e < cnt);
+    for (int e = E - 1; e >= 0; --e) inb.push(e, e < cnt);   // every block is a candidate
   }
 
   // ---- 3. resolve the candidates
@@ -320,11 +365,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, cons
   if (grid && krem == c0) {
 #pragma unroll
     for (int i = 0; i < ElemBits<E>::W; ++i) keep.w[i] |= inb.w[i];   // B0 kept whole
-  } else {
-    uint32_t T = 0u, M = 0xFFFFFFFFu;
-    bool done = false;
-    if (c0 <= (uint32_t)kCandCap) {
-      // stage the candidates (wave-aggregated append), then rank them
+  } else if (ranked) {
+    if (!kFuseStage) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const bool mine = inb.test(e);
@@ -339,55 +381,52 @@ __global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, cons
             cand_s[wbase + slot] = u32x2{score_key(QSA_X(e)), (uint32_t)(beg + e)};
         }
       }
-      __syncthreads();
-      if (tid < (int)c0) {
-        const u32x2 me = cand_s[tid];
-        uint32_t higher = 0u, ahead = 0u;
-        for (int j = 0; j < (int)c0; ++j) {
-          const u32x2 o = cand_s[j];
-          higher += o.x > me.x;
-          ahead += (o.x == me.x) & (o.y < me.y);
-        }
-        if (higher + ahead == krem - 1u) {
-          s_T = me.x;
-          s_need = krem - higher;
-        }
+    }
+    __syncthreads();
+    if (tid < (int)c0) {
+      const u32x2 me = cand_s[tid];
+      uint32_t ahead = 0u;
+      for (int j = 0; j < (int)c0; ++j) {
+        const u32x2 o = cand_s[j];
+        ahead += (o.x > me.x) | ((o.x == me.x) & (o.y < me.y));
       }
-      __syncthreads();
-      T = s_T;
-      need = s_need;
-      done = true;
+      if (ahead < krem) atomicOr(&keepmap[me.y >> 5], 1u << (me.y & 31));
+    }
+    __syncthreads();
+    if (E == 64) {
+      keep.w[0] |= keepmap[2 * tid];
+      keep.w[ElemBits<E>::W - 1] |= keepmap[2 * tid + 1];
     } else {
-      // many candidates: done at once if they all tie
-      uint32_t bmax = 0u, bmin = 0xFFFFFFFFu;
+      const uint32_t word = keepmap[(tid * E) >> 5] >> ((tid * E) & 31);
+      keep.w[0] |= E == 32 ? word : (word & ((1u << (E & 31)) - 1u));
+    }
+  } else {
+    // many candidates (or no grid): done at once if they all tie
+    uint32_t bmax = 0u, bmin = 0xFFFFFFFFu;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (inb.test(e)) {
-          const uint32_t key = score_key(QSA_X(e));
-          bmax = max(bmax, key);
-          bmin = min(bmin, key);
-        }
-      }
-      bmax = wave_max_u32(bmax);
-      bmin = wave_min_u32(bmin);
-      if (lane == 0) {
-        red2_s[wave] = bmax;
-        red2_s[NW + wave] = bmin;
-      }
-      __syncthreads();
-      bmax = lds_slots_max(red2_s, NW);
-      bmin = lds_slots_min(red2_s + NW, NW);
-      if (bmax == bmin) {
-        T = bmax;
-        need = krem;
-        done = true;
+    for (int e = 0; e < E; ++e) {
+      if (inb.test(e)) {
+        const uint32_t key = score_key(QSA_X(e));
+        bmax = max(bmax, key);
+        bmin = min(bmin, key);
       }
     }
-    if (!done) {
+    bmax = wave_max_u32(bmax);
+    bmin = wave_min_u32(bmin);
+    if (lane == 0) {
+      red2_s[wave] = bmax;
+      red2_s[NW + wave] = bmin;
+    }
+    __syncthreads();
+    bmax = lds_slots_max(red2_s, NW);
+    bmin = lds_slots_min(red2_s + NW, NW);
+    if (bmax == bmin) {
+      ties = inb;         // all tie: the lowest indices are kept
+      need = krem;
+    } else {
       // MSB-first radix passes (11, 11, 10 key bits) over the candidates;
       // stop once the threshold bin is taken whole
       uint32_t prefix = 0u, pmask = 0u;
-      int h = grid ? 1 : 0;
 #pragma unroll 1
       for (int pass = 0; pass < 3; ++pass) {
         const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
@@ -411,19 +450,16 @@ __global__ __launch_bounds__(kSelectThreads) void select_reg_kernel(Meta m, cons
         h ^= 1;
         if (krem == bin_count) break;
       }
-      T = prefix;
-      M = pmask;
+      // split the candidates around the threshold (key & pmask) == prefix
+      const uint32_t T = fresh_uniform(prefix), M = fresh_uniform(pmask);
       need = krem;
-    }
-    // split the candidates around the threshold
-    T = fresh_uniform(T);
-    M = fresh_uniform(M);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if (inb.test(e)) {
-        const uint32_t km = score_key(QSA_X(e)) & M;
-        keep.set(e, km > T);
-        ties.set(e, km == T);
+      for (int e = 0; e < E; ++e) {
+        if (inb.test(e)) {
+          const uint32_t km = score_key(QSA_X(e)) & M;
+          keep.set(e, km > T);
+          ties.set(e, km == T);
+        }
       }
     }
   }
@@ -712,18 +748,27 @@ __global__ __launch_bounds__(256) void build_index_kernel(Meta m, const int32_t*
   if (threadIdx.x == 0) n_pos[q] = np;
 }
 
+#ifndef QSA_SELECT_NT16K
+#define QSA_SELECT_NT16K 1024
+#endif
+
 template <bool kWritePos>
 static void launch_select_t(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel, int32_t* n_sel,
                             int32_t* pos, int32_t* n_pos, int width, hipStream_t stream) {
-  const dim3 grid(m.num_q), block(kSelectThreads);
-  if (m.max_blocks <= 16 * kSelectThreads)
-    select_reg_kernel<16, kWritePos><<<grid, block, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
+  const dim3 grid(m.num_q);
+  constexpr int NT16 = QSA_SELECT_NT16K;                 // threads per query for rows up to 16,384 blocks
+  if (m.max_blocks <= 16384)
+    select_reg_kernel<16384 / NT16, NT16, kWritePos><<<grid, NT16, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos,
+                                                                               n_pos, width);
   else if (m.max_blocks <= 32 * kSelectThreads)
-    select_reg_kernel<32, kWritePos><<<grid, block, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
+    select_reg_kernel<32, kSelectThreads, kWritePos>
+        <<<grid, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
   else if (m.max_blocks <= 64 * kSelectThreads)
-    select_reg_kernel<64, kWritePos><<<grid, block, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
+    select_reg_kernel<64, kSelectThreads, kWritePos>
+        <<<grid, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
   else
-    select_stream_kernel<kWritePos><<<grid, block, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
+    select_stream_kernel<kWritePos>
+        <<<grid, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
 }
 
 hipError_t launch_select(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel, int32_t* n_sel,
