@@ -46,19 +46,27 @@ def test_config_parity(name):
     torch.cuda.empty_cache()
 
 
-def test_scores_bit_exact_at_50k():
-    """Stage call a1 at full size: every FP32 score bit-identical."""
+@pytest.mark.parametrize("name", ["mtp50k", "mtp50k_b32_fp8", "ragged64"])
+def test_scores_bit_exact_full_size(name):
+    """Stage call a1 at full size (the batched workloads take the streaming
+    score kernel): every FP32 score bit-identical, nothing written past a
+    request's full blocks."""
     import block_sparse_attention_qsa_amd as qsa
     need_gpu()
-    w = make_workload("mtp50k")
+    w = make_workload(name)
     dev = upload(w)
     b = qsa.Batch(w.q_start, w.seq_len, w.kv_start, w.blk_start)
-    scores = torch.zeros((w.num_q, b.max_blocks), dtype=torch.float32, device="cuda")
-    say("qsa_score mtp50k")
+    scores = torch.full((w.num_q, b.max_blocks), -7.0, dtype=torch.float32, device="cuda")
+    say("qsa_score", name)
     qsa.qsa_score(b, dev["idx_q"], dev["ckeys"], scores)
     torch.cuda.synchronize()
     s = scores.cpu().numpy()
-    b0 = int(w.blk_start[0])
-    for qi in range(4):
-        ref = oracle.block_scores(w.idx_q[qi], w.ckeys[b0:b0 + 12500])
-        assert np.array_equal(s[qi, :12500].view(np.uint32), ref.view(np.uint32))
+    for r in range(w.num_req):
+        b0, nblk = int(w.blk_start[r]), int(w.seq_len[r]) // 4
+        for qi in range(int(w.q_start[r]), int(w.q_start[r + 1])):
+            ref = oracle.block_scores(w.idx_q[qi], w.ckeys[b0:b0 + nblk])
+            assert np.array_equal(s[qi, :nblk].view(np.uint32), ref.view(np.uint32)), (name, r, qi)
+            assert np.all(s[qi, nblk:] == -7.0), (name, r, qi)
+    del dev
+    gc.collect()
+    torch.cuda.empty_cache()
