@@ -18,7 +18,7 @@ from typing import Optional
 import torch
 
 __all__ = ["QsaError", "Batch", "lib", "abi_version", "status_string", "workspace_bytes", "alloc_workspace",
-           "qsa_score", "qsa_select_topk", "qsa_build_index", "qsa_sparse_attn", "qsa_decode",
+           "qsa_score", "qsa_select_topk", "qsa_build_index", "qsa_sparse_attn", "qsa_decode", "qsa_compress_keys",
            "BLOCK", "TOPK", "WIDTH", "INDEX_DIM", "HEAD_DIM", "KV_BF16", "KV_FP8_E4M3", "OUT_F32", "OUT_BF16"]
 
 BLOCK = 4
@@ -40,7 +40,8 @@ class QsaError(RuntimeError):
 class _CBatch(ctypes.Structure):
     _fields_ = [("num_req", ctypes.c_int32), ("num_q", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
                 ("q_start", ctypes.c_void_p), ("seq_len", ctypes.c_void_p), ("kv_start", ctypes.c_void_p),
-                ("blk_start", ctypes.c_void_p)]
+                ("blk_start", ctypes.c_void_p), ("page_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+                ("pages_per_req", ctypes.c_int32)]
 
 
 _lib = None
@@ -61,6 +62,7 @@ _SIGNATURES = {
                                        _P, _SZ, _P]),
     "qsa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _F, _P, _I32,
                                   _P, _P, _P, _P, _P, _SZ, _P]),
+    "qsa_compress_keys": (ctypes.c_int, [_P, _P, _P, _P, _P]),
 }
 
 
@@ -123,10 +125,14 @@ class Batch:
     Host arrays (numpy / CPU tensors / lists) are copied to `device` and the
     host scalars (num_req, num_q, max_blocks) derived from them.  Device int32
     tensors are used as they are and then num_q and max_blocks must be given.
+    A paged KV cache is described by page_table ([num_req, pages_per_req]
+    int32, physical page of each logical page) and page_size (a multiple of
+    4); kv_start is then unused and may be None.
     """
 
     def __init__(self, q_start, seq_len, kv_start, blk_start, *, num_q: Optional[int] = None,
-                 max_blocks: Optional[int] = None, device="cuda"):
+                 max_blocks: Optional[int] = None, page_table=None, page_size: Optional[int] = None,
+                 device="cuda"):
         def to_dev(x):
             if isinstance(x, torch.Tensor) and x.is_cuda:
                 if x.dtype != torch.int32 or not x.is_contiguous():
@@ -144,13 +150,28 @@ class Batch:
             raise QsaError("num_q and max_blocks are required with device metadata")
         self.q_start = to_dev(q_start)
         self.seq_len = to_dev(seq_len)
-        self.kv_start = to_dev(kv_start)
+        self.kv_start = None if kv_start is None else to_dev(kv_start)
         self.blk_start = to_dev(blk_start)
         self.num_req = int(self.seq_len.shape[0])
         self.num_q = int(num_q)
         self.max_blocks = int(max_blocks)
-        self._c = _CBatch(self.num_req, self.num_q, self.max_blocks, self.q_start.data_ptr(),
-                          self.seq_len.data_ptr(), self.kv_start.data_ptr(), self.blk_start.data_ptr())
+        self.page_table = None
+        self.page_size = 0
+        pages_per_req = 0
+        if page_table is not None:
+            if page_size is None:
+                raise QsaError("page_size is required with a page table")
+            self.page_table = to_dev(page_table)
+            if self.page_table.dim() != 2 or self.page_table.shape[0] != self.num_req:
+                raise QsaError("page_table must be [num_req, pages_per_req]")
+            self.page_size = int(page_size)
+            pages_per_req = int(self.page_table.shape[1])
+        elif self.kv_start is None:
+            raise QsaError("kv_start is required without a page table")
+        ptr = lambda t: None if t is None else t.data_ptr()
+        self._c = _CBatch(self.num_req, self.num_q, self.max_blocks, ptr(self.q_start), ptr(self.seq_len),
+                          ptr(self.kv_start), ptr(self.blk_start), ptr(self.page_table), self.page_size,
+                          pages_per_req)
 
     @property
     def c(self):
@@ -269,3 +290,15 @@ def qsa_decode(batch: Batch, idx_q, ckeys, q, k_cache, v_cache, out, workspace, 
                             _ptr(k_scale), _ptr(v_scale), hq, hkv, k, sm, _ptr(out), _out_dtype(out),
                             _ptr(sel), _ptr(n_sel), _ptr(pos), _ptr(n_pos), _ptr(workspace),
                             workspace.numel(), _stream(stream)), "qsa_decode")
+
+
+def qsa_compress_keys(batch: Batch, prev_len, tok_keys, ckeys, stream=None) -> None:
+    """Compressed keys of the blocks completed since prev_len (see qsa.h)."""
+    _dev(prev_len, "prev_len", (torch.int32,), (batch.num_req,))
+    _dev(tok_keys, "tok_keys", _BF16)
+    _dev(ckeys, "ckeys", _BF16)
+    for name, t in (("tok_keys", tok_keys), ("ckeys", ckeys)):
+        if t.dim() != 2 or t.shape[1] != INDEX_DIM:
+            raise QsaError(f"{name} must be [rows, {INDEX_DIM}]")
+    _check(lib().qsa_compress_keys(batch.c, _ptr(prev_len), _ptr(tok_keys), _ptr(ckeys), _stream(stream)),
+           "qsa_compress_keys")

@@ -40,10 +40,15 @@ WsLayout ws_layout(int num_q, int max_blocks, int hq, int hkv, int k) {
 
 qsa_status check_batch(const qsa_batch* b) {
   if (!b) return QSA_ERR_NULL;
-  if (!b->q_start || !b->seq_len || !b->kv_start || !b->blk_start) return QSA_ERR_NULL;
+  if (!b->q_start || !b->seq_len || !b->blk_start) return QSA_ERR_NULL;
+  if (!b->page_table && !b->kv_start) return QSA_ERR_NULL;
   if (b->num_req < 1 || b->num_req > QSA_MAX_REQUESTS) return QSA_ERR_SHAPE;
   if (b->num_q < b->num_req || b->num_q > QSA_MAX_Q_PER_REQ * b->num_req) return QSA_ERR_SHAPE;
   if (b->max_blocks < 0 || b->max_blocks > QSA_MAX_BLOCKS) return QSA_ERR_SHAPE;
+  if (b->page_table) {
+    if (b->page_size < QSA_BLOCK || b->page_size % QSA_BLOCK != 0 || b->pages_per_req < 1) return QSA_ERR_SHAPE;
+    if ((int64_t)b->page_size * b->pages_per_req > INT32_MAX) return QSA_ERR_SHAPE;
+  }
   return QSA_OK;
 }
 
@@ -81,6 +86,9 @@ Meta meta_of(const qsa_batch* b) {
   m.seq_len = b->seq_len;
   m.kv_start = b->kv_start;
   m.blk_start = b->blk_start;
+  m.page_table = b->page_table;
+  m.page_size = b->page_table ? b->page_size : 0;
+  m.pages_per_req = b->page_table ? b->pages_per_req : 0;
   return m;
 }
 
@@ -178,6 +186,13 @@ qsa_status qsa_sparse_attn(const qsa_batch* batch, const void* q, const void* k_
   a.partials = reinterpret_cast<float*>(base + w.partials);
   a.counters = reinterpret_cast<uint32_t*>(base + w.counters);
   return launched(qsa::launch_attn(meta_of(batch), a, stream));
+}
+
+qsa_status qsa_compress_keys(const qsa_batch* batch, const int32_t* prev_len, const void* tok_keys, void* ckeys,
+                             hipStream_t stream) {
+  QSA_TRY(check_batch(batch));
+  if (!prev_len || !tok_keys || !ckeys) return QSA_ERR_NULL;
+  return launched(qsa::launch_compress_keys(meta_of(batch), prev_len, tok_keys, ckeys, stream));
 }
 
 qsa_status qsa_decode(const qsa_batch* batch, const void* idx_q, const void* ckeys, const void* q,

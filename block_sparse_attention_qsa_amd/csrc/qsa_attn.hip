@@ -243,7 +243,6 @@ template <bool kFp8, bool kOutBf16>
 __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   constexpr int D = QSA_HEAD_DIM;
   constexpr int EB = kFp8 ? 1 : 2;            // bytes per KV element
-  constexpr int kGroupOut = 4;                // merged outputs per thread per round
   __shared__ float o_s[kAttnWaves][16][kOStride];
   __shared__ float m_s[kAttnWaves][16], l_s[kAttnWaves][16];
   __shared__ float w_s[16];

@@ -12,7 +12,19 @@ struct Meta {
   const int32_t* seq_len;
   const int32_t* kv_start;
   const int32_t* blk_start;
+  const int32_t* page_table;   // nullptr: contiguous requests from kv_start
+  int page_size, pages_per_req;
 };
+
+// KV slot of token t of request r: kv_start[r] + t, or through the page table
+// (page_size a multiple of 4, so a block's 4 tokens are 4 consecutive slots).
+// The logical page is clamped to the table row.
+__device__ __forceinline__ int32_t token_slot(const Meta& m, int r, int t) {
+  if (m.page_table == nullptr) return m.kv_start[r] + t;
+  int p = t / m.page_size;
+  p = p < m.pages_per_req ? p : m.pages_per_req - 1;
+  return m.page_table[(int64_t)r * m.pages_per_req + p] * m.page_size + t % m.page_size;
+}
 
 struct AttnArgs {
   const void* q;            // BF16 [num_q][Hq][128]
@@ -40,6 +52,8 @@ hipError_t launch_select(const Meta& m, const float* scores, int64_t ld, int k, 
 hipError_t launch_build_index(const Meta& m, const int32_t* sel, const int32_t* n_sel, int k, int32_t* pos,
                               int32_t* n_pos, int width, hipStream_t stream);
 hipError_t launch_attn(const Meta& m, const AttnArgs& a, hipStream_t stream);
+hipError_t launch_compress_keys(const Meta& m, const int32_t* prev_len, const void* tok_keys, void* ckeys,
+                                hipStream_t stream);
 
 // Bytes of split partials the attention needs for this geometry.
 size_t attn_partial_bytes(int num_q, int num_kv_heads, int group, int width);

@@ -236,7 +236,8 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(Meta m, const float* __r
   if (nf > m.max_blocks) nf = m.max_blocks;
   if (nf > E * NT) nf = E * NT;                      // launcher picks E * NT >= max_blocks
   const int pl = L & 3;
-  const int kv0 = m.kv_start[r];
+  const bool paged = m.page_table != nullptr;
+  const int kv0 = paged ? 0 : m.kv_start[r];
   int32_t* sel_row = sel + (int64_t)q * k;
   int32_t* pos_row = kWritePos ? pos + (int64_t)q * width : nullptr;
 
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(Meta m, const float* __r
     for (int i = tid; i < k; i += NT) sel_row[i] = i < nf ? i : -1;
     if (kWritePos) {
       const int np = 4 * nf + pl;
-      for (int i = tid; i < width; i += NT) pos_row[i] = i < np ? kv0 + i : -1;
+      for (int i = tid; i < width; i += NT) pos_row[i] = i < np ? (paged ? token_slot(m, r, i) : kv0 + i) : -1;
     }
     if (tid == 0) {
       n_sel[q] = nf;
@@ -504,8 +505,12 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(Meta m, const float* __r
     const int np = 4 * ns + pl;
     for (int i = tid; i < width; i += NT) {
       int v = -1;
-      if (i < 4 * ns) v = kv0 + 4 * min(max(sel_s[i >> 2], 0), nf - 1) + (i & 3);
-      else if (i < np) v = kv0 + 4 * nf + (i - 4 * ns);
+      if (i < 4 * ns) {
+        const int b = min(max(sel_s[i >> 2], 0), nf - 1);
+        v = (paged ? token_slot(m, r, 4 * b) : kv0 + 4 * b) + (i & 3);
+      } else if (i < np) {
+        v = (paged ? token_slot(m, r, 4 * nf) : kv0 + 4 * nf) + (i - 4 * ns);
+      }
       pos_row[i] = v;
     }
   }
@@ -537,7 +542,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_stream_kernel(Meta m, c
   int nf = L >> 2;
   if (nf > m.max_blocks) nf = m.max_blocks;
   const int pl = L & 3;
-  const int kv0 = m.kv_start[r];
+  const bool paged = m.page_table != nullptr;
+  const int kv0 = paged ? 0 : m.kv_start[r];
   const float* srow = scores + (int64_t)q * ld;
   int32_t* sel_row = sel + (int64_t)q * k;
   int32_t* pos_row = kWritePos ? pos + (int64_t)q * width : nullptr;
@@ -547,7 +553,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_stream_kernel(Meta m, c
     for (int i = tid; i < k; i += NT) sel_row[i] = i < nf ? i : -1;
     if (kWritePos) {
       const int np = 4 * nf + pl;
-      for (int i = tid; i < width; i += NT) pos_row[i] = i < np ? kv0 + i : -1;
+      for (int i = tid; i < width; i += NT) pos_row[i] = i < np ? (paged ? token_slot(m, r, i) : kv0 + i) : -1;
     }
     if (tid == 0) {
       n_sel[q] = nf;
@@ -698,7 +704,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_stream_kernel(Meta m, c
       if (take) {
         sel_row[o] = i;
         if (kWritePos) {
-          const int p0 = kv0 + 4 * i;
+          const int p0 = paged ? token_slot(m, r, 4 * i) : kv0 + 4 * i;
           pos_row[4 * o + 0] = p0;
           pos_row[4 * o + 1] = p0 + 1;
           pos_row[4 * o + 2] = p0 + 2;
@@ -711,7 +717,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_stream_kernel(Meta m, c
   if (kWritePos) {
     for (int i = 4 * k + tid; i < width; i += NT) {
       const int t = i - 4 * k;
-      pos_row[i] = t < pl ? kv0 + 4 * nf + t : -1;
+      pos_row[i] = t < pl ? (paged ? token_slot(m, r, 4 * nf) : kv0 + 4 * nf) + t : -1;
     }
   }
   if (tid == 0) {
@@ -720,6 +726,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_stream_kernel(Meta m, c
   }
 }
 
+// Position buffer from a selection: of the first min(n_sel, k) entries of
+// the (ascending) selection row, those below nf are used; later ones are not
+// full blocks of this query and are dropped, so that a selection made for a
+// longer query can be reused.
 __global__ __launch_bounds__(256) void build_index_kernel(Meta m, const int32_t* __restrict__ sel,
                                                           const int32_t* __restrict__ n_sel, int k,
                                                           int32_t* __restrict__ pos, int32_t* __restrict__ n_pos,
@@ -732,17 +742,26 @@ __global__ __launch_bounds__(256) void build_index_kernel(Meta m, const int32_t*
   int nf = L >> 2;
   if (nf > m.max_blocks) nf = m.max_blocks;
   const int pl = L & 3;
-  const int kv0 = m.kv_start[r];
-  int ns = n_sel[q];
-  ns = ns < 0 ? 0 : (ns > k ? k : ns);
-  const int np = 4 * ns + pl;
+  const bool paged = m.page_table != nullptr;
+  const int kv0 = paged ? 0 : m.kv_start[r];
+  int given = n_sel[q];
+  given = given < 0 ? 0 : (given > k ? k : given);
   const int32_t* srow = sel + (int64_t)q * k;
+  // 256 threads, k <= 512: entries tid and tid + 256 per thread
+  const int i0 = threadIdx.x, i1 = threadIdx.x + 256;
+  const bool ok0 = i0 < given && srow[i0] >= 0 && srow[i0] < nf;
+  const bool ok1 = i1 < given && srow[i1] >= 0 && srow[i1] < nf;
+  const int ns = __syncthreads_count(ok0) + __syncthreads_count(ok1);
+  const int np = 4 * ns + pl;
   int32_t* prow = pos + (int64_t)q * width;
   for (int i = threadIdx.x; i < width; i += blockDim.x) {
-    int v;
-    if (i < 4 * ns) v = kv0 + 4 * srow[i >> 2] + (i & 3);
-    else if (i < np) v = kv0 + 4 * nf + (i - 4 * ns);
-    else v = -1;
+    int v = -1;
+    if (i < 4 * ns) {
+      const int b = srow[i >> 2];
+      v = (paged ? token_slot(m, r, 4 * b) : kv0 + 4 * b) + (i & 3);
+    } else if (i < np) {
+      v = (paged ? token_slot(m, r, 4 * nf) : kv0 + 4 * nf) + (i - 4 * ns);
+    }
     prow[i] = v;
   }
   if (threadIdx.x == 0) n_pos[q] = np;

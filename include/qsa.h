@@ -33,8 +33,12 @@
  * request's cached tokens including this step's verify tokens, so verify query
  * j (0-based) has causal length L = seq_len[r] - nq_r + 1 + j, nf = L / 4 full
  * blocks and a partial block of L % 4 tokens (nothing when L % 4 == 0).
- * Token t of request r lives in KV slot kv_start[r] + t; the compressed key of
- * its full block b is row blk_start[r] + b of the key array.
+ * Token t of request r lives in KV slot slot_r(t) = kv_start[r] + t, or, when
+ * the batch carries a page table (paged KV cache), in slot
+ *   slot_r(t) = page_table[r * pages_per_req + t / page_size] * page_size + t % page_size
+ * with page_size a multiple of 4, so the 4 tokens of a block always sit in 4
+ * consecutive slots.  The compressed key of full block b is row
+ * blk_start[r] + b of the key array (keys are not paged).
  */
 #ifndef QSA_H
 #define QSA_H
@@ -47,7 +51,7 @@
 extern "C" {
 #endif
 
-#define QSA_ABI_VERSION 1
+#define QSA_ABI_VERSION 2
 #define QSA_BLOCK 4                                  /* tokens per micro-block            */
 #define QSA_TOPK 512                                 /* max full blocks kept per query    */
 #define QSA_WIDTH (QSA_BLOCK * QSA_TOPK + QSA_BLOCK - 1) /* 2,051 position-buffer entries */
@@ -79,6 +83,12 @@ typedef struct {
   const int32_t* seq_len;    /* [dev]  int32[B], cached tokens incl. verify tokens     */
   const int32_t* kv_start;   /* [dev]  int32[B], first KV slot of request r            */
   const int32_t* blk_start;  /* [dev]  int32[B], first compressed-key row of request r */
+  const int32_t* page_table; /* [dev]  int32[B][pages_per_req] physical page of each
+                                       logical page, or NULL for contiguous requests
+                                       (then kv_start is used and the two fields below
+                                       are ignored)                                  */
+  int32_t page_size;         /* [host] tokens per page, a positive multiple of 4       */
+  int32_t pages_per_req;     /* [host] row stride of page_table, >= 1                  */
 } qsa_batch;
 
 /* Version of this ABI (QSA_ABI_VERSION). */
@@ -115,11 +125,17 @@ qsa_status qsa_select_topk(const qsa_batch* batch, const float* scores, int64_t 
                            int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
-/* a3 - position buffer.  For query q of request r with n = n_sel[q] kept blocks:
- *   pos[q][4i + t] = kv_start[r] + 4 * sel[q][i] + t      (i < n, t < 4)
- *   pos[q][4n + t] = kv_start[r] + 4 * nf + t             (t < L % 4, the partial block)
+/* a3 - position buffer.  For query q of request r, of the first min(n_sel[q], k)
+ * entries of sel[q] (ascending, as qsa_select_topk writes them) the n entries
+ * below nf - the blocks that are full for this query - are used:
+ *   pos[q][4i + t] = slot_r(4 * sel[q][i] + t)            (i < n, t < 4)
+ *   pos[q][4n + t] = slot_r(4 * nf + t)                   (t < L % 4, the partial block)
  *   pos[q][i]      = -1                                   (i >= n_pos[q], up to 4k+3)
- * n_pos[q] = 4n + L % 4.  pos [dev] int32 [num_q][4k+3]; n_pos [dev] int32 [num_q]. */
+ * n_pos[q] = 4n + L % 4.  pos [dev] int32 [num_q][4k+3]; n_pos [dev] int32 [num_q].
+ * Entries at or past nf are dropped rather than trusted, so a selection made
+ * at an earlier step can be reused when later MTP draft steps (or a step
+ * after rejected drafts) attend with other lengths, as the arex-research.com
+ * article (four optimisations, MTP reuse) describes for draft steps. */
 qsa_status qsa_build_index(const qsa_batch* batch, const int32_t* sel, const int32_t* n_sel,
                            int32_t k, int32_t* pos, int32_t* n_pos, hipStream_t stream);
 
@@ -138,6 +154,20 @@ qsa_status qsa_sparse_attn(const qsa_batch* batch, const void* q, const void* k_
                            const int32_t* pos, const int32_t* n_pos, int32_t width,
                            float sm_scale, void* out, int32_t out_dtype, void* ws,
                            size_t ws_bytes, hipStream_t stream);
+
+/* The step before a1: compressed keys of the blocks completed by newly
+ * appended tokens.  For request r, every block b with
+ * prev_len[r] <= 4b + 3 < seq_len[r] gets
+ *   ckeys[blk_start[r] + b][d] = bf16_rne( (k(4b) + k(4b+1) + k(4b+2) + k(4b+3)) / 4 )
+ * where k(t) = tok_keys[slot_r(t)][d] is the BF16 per-token index key, the sum
+ * is taken in FP64 in that order and rounded once to BF16 (nearest, ties to
+ * even).  The pages compute a compressed index key for every 4-token block
+ * (arex-research.com article, four optimisations, item 1) without stating the
+ * compression; the mean of the block's token keys is this library's stand-in.
+ * prev_len [dev] int32 [B] (0 <= prev_len[r] <= seq_len[r]); tok_keys [dev] BF16
+ * [slots][128]; ckeys [dev] BF16 [rows][128].  Other rows are not written. */
+qsa_status qsa_compress_keys(const qsa_batch* batch, const int32_t* prev_len, const void* tok_keys,
+                             void* ckeys, hipStream_t stream);
 
 /* a1..a4 in one call, the whole decode / MTP-verify step of one QSA layer for
  * the batch: scores, selection and positions live in the workspace, and

@@ -27,12 +27,21 @@ Where the pages leave a step open, this file takes the plain reading:
     (verify tokens included) sees the causal prefix L = seq_len - nq + 1 + j;
     its full blocks are [0, L // 4) and its partial block is the last L % 4
     tokens (nothing is kept when L % 4 == 0);
-  * a position is the physical KV slot kv_start + token index;
+  * a position is the physical KV slot of the token: kv_start + token index,
+    or, with a paged cache, page_table[token // page_size] * page_size +
+    token % page_size (page_size a multiple of 4);
+  * a selection reused at another length keeps only its blocks that are full
+    for the new query (later MTP draft steps reuse earlier positions: 10100.com
+    article, section on the third optimisation);
+  * the compressed key of a block (the pages do not give the rule) is the mean
+    of its four per-token index keys, rounded once to BF16, nearest-even;
   * softmax scale is passed in (1/sqrt(128) for head_dim 128); GQA maps query
     head h to KV head h // (Hq / Hkv);
   * FP8 is OCP E4M3FN with one FP32 scale per KV head for K and one for V.
 """
 from __future__ import annotations
+
+from fractions import Fraction
 
 import numpy as np
 
@@ -92,22 +101,97 @@ def select_blocks(scores, k: int = TOPK) -> np.ndarray:
     return np.sort(order[:k]).astype(np.int64)
 
 
-def build_positions(sel, L: int, kv_start: int, k: int = TOPK):
+def token_slots(t, kv_start: int = 0, page_row=None, page_size: int | None = None) -> np.ndarray:
+    """Physical KV slots of logical token indices t of one request."""
+    t = np.asarray(t, dtype=np.int64)
+    if page_row is None:
+        return t + int(kv_start)
+    page_row = np.asarray(page_row, dtype=np.int64)
+    return page_row[t // page_size] * page_size + t % page_size
+
+
+def build_positions(sel, L: int, kv_start: int, k: int = TOPK, page_row=None, page_size: int | None = None):
     """Fixed-width position buffer of one query and its valid length.
 
-    Each kept block b contributes its four slots 4b..4b+3, in block order; the
-    partial block [4 * (L // 4), L) follows; the rest of the 4k+3 entries is -1.
-    Slots are offset by the request's first KV slot.
+    Each kept block b that is full for this query (b < L // 4) contributes the
+    slots of its tokens 4b..4b+3, in block order; the partial block's tokens
+    [4 * (L // 4), L) follow; the rest of the 4k+3 entries is -1.
     """
     sel = np.asarray(sel, dtype=np.int64)
     nf = L // BLOCK
+    sel = sel[(sel >= 0) & (sel < nf)]
     full = (BLOCK * sel[:, None] + np.arange(BLOCK)[None, :]).reshape(-1)
     partial = np.arange(BLOCK * nf, L, dtype=np.int64)
-    p = np.concatenate([full, partial]) + int(kv_start)
+    p = token_slots(np.concatenate([full, partial]), kv_start, page_row, page_size)
     width = BLOCK * k + BLOCK - 1
     out = np.full(width, -1, dtype=np.int64)
     out[:p.shape[0]] = p
     return out, int(p.shape[0])
+
+
+BF16_MAX = Fraction(2 - Fraction(1, 128)) * Fraction(2) ** 127
+
+
+def bf16_bits_round_exact(value: Fraction, negative_zero: bool = False) -> int:
+    """BF16 bit pattern of an exact rational, rounded to nearest, ties to even
+    (IEEE round-to-nearest: beyond the largest finite value it becomes inf).
+
+    A BF16 number is s * m * 2^(e-7) with an 8-bit significand m in [128, 256)
+    for normal values (e >= -126) and the fixed unit 2^-133 below 2^-126; the
+    value is divided by the unit of its binade, rounded half-to-even to an
+    integer and scaled back.  A zero result is -0 only when negative_zero.
+    """
+    neg = value < 0
+    a = -value if neg else value
+    if a == 0:
+        return 0x8000 if negative_zero else 0x0000
+    e = int(np.frexp(float(a))[1]) - 1
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)
+    unit = Fraction(2) ** (e - 7)
+    n = a / unit
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    r = fl * unit
+    if r > BF16_MAX:
+        bits = 0x7F80
+    else:
+        bits = int(np.array([float(r)], dtype=np.float32).view(np.uint32)[0]) >> 16
+    return bits | (0x8000 if neg else 0)
+
+
+def compress_block_key(token_key_bits) -> np.ndarray:
+    """Compressed index key of one 4-token block from its tokens' BF16 keys.
+
+    token_key_bits: uint16 [4, d].  Each dimension is the exact mean of the
+    four values, rounded once to BF16 (nearest, ties to even); a zero mean is
+    -0 only when all four values are -0 (as an IEEE sum in token order gives).
+    """
+    bits = np.asarray(token_key_bits, dtype=np.uint16)
+    vals = bf16_to_f64(bits)
+    out = np.empty(bits.shape[1], dtype=np.uint16)
+    for dd in range(bits.shape[1]):
+        total = sum(Fraction(float(v)) for v in vals[:, dd])
+        all_neg_zero = bool(np.all(bits[:, dd] == 0x8000))
+        out[dd] = bf16_bits_round_exact(total / 4, negative_zero=all_neg_zero)
+    return out
+
+
+def compress_new_keys(seq_len: int, prev_len: int, tok_keys, kv_start: int = 0, page_row=None,
+                      page_size: int | None = None) -> dict:
+    """Keys of the blocks completed by the tokens appended since prev_len:
+    {block index b: uint16 [d]} for every b with prev_len <= 4b + 3 < seq_len."""
+    out = {}
+    prev_len = min(max(int(prev_len), 0), int(seq_len))
+    for b in range(prev_len // BLOCK, int(seq_len) // BLOCK):
+        slots = token_slots(np.arange(BLOCK * b, BLOCK * b + BLOCK), kv_start, page_row, page_size)
+        out[b] = compress_block_key(np.asarray(tok_keys)[slots])
+    return out
 
 
 def sparse_attention(q_heads, k_rows, v_rows, sm_scale: float) -> np.ndarray:
@@ -138,13 +222,15 @@ def _dequant(cache, rows, kv_dtype, scale):
 
 def decode(q_start, seq_len, kv_start, blk_start, idx_q, ckeys, q, k_cache, v_cache,
            kv_dtype: str, k_scale=None, v_scale=None, k: int = TOPK, sm_scale: float | None = None,
-           want_scores: bool = True, queries=None) -> dict:
+           want_scores: bool = True, queries=None, page_table=None, page_size: int | None = None) -> dict:
     """Run score -> top-k -> positions -> gather attention for every query.
 
     Returns a dict with per-query 'scores' (list of float32 arrays, if asked),
     'sel' int32 [num_q, k] (-1 padded), 'n_sel', 'pos' int32 [num_q, 4k+3]
     (-1 padded), 'n_pos', and 'out' float64 [num_q, Hq, d].  `queries` limits
     the work to a subset of query indices (other rows stay zero / -1).
+    With page_table ([num_req][pages] int) and page_size, token slots go
+    through the page table instead of kv_start.
     """
     q_start = np.asarray(q_start, np.int64)
     num_q = int(q_start[-1])
@@ -172,7 +258,10 @@ def decode(q_start, seq_len, kv_start, blk_start, idx_q, ckeys, q, k_cache, v_ca
             b0 = int(blk_start[r])
             s = block_scores(idx_q[qi], ckeys[b0:b0 + nf])
             sel = select_blocks(s, k)
-            pos, n_pos = build_positions(sel, L, int(kv_start[r]), k)
+            if page_table is None:
+                pos, n_pos = build_positions(sel, L, int(kv_start[r]), k)
+            else:
+                pos, n_pos = build_positions(sel, L, 0, k, page_table[r], page_size)
             rows = pos[:n_pos]
             kr = _dequant(k_cache, rows, kv_dtype, k_scale)
             vr = _dequant(v_cache, rows, kv_dtype, v_scale)

@@ -19,7 +19,7 @@ from fractions import Fraction
 import numpy as np
 import torch
 
-from workloads import make_custom, bf16_bits_from_f32, fp8_e4m3fn_bits_from_f32
+from workloads import make_custom, bf16_bits_from_f32, fp8_e4m3fn_bits_from_f32, paged_layout
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -319,6 +319,115 @@ def check_attention_special_cases(orc):
     assert np.array_equal(o[0], vr[n - 1, 0, :])
 
 
+# ---------------------------------------------------------------- paged KV, reuse
+def check_paged_positions(orc):
+    """Page-table slots: an identity table reproduces contiguous slots from 0;
+    a permuted table maps every logical token t to table[t // P] * P + t % P,
+    keeps each block's four slots consecutive, and a paged decode over caches
+    re-laid out that way gives bit-identical outputs to the contiguous one."""
+    rng = np.random.default_rng(41)
+    for P in (4, 16, 64):
+        for L in (3, 4, 5, 2051, 2052, 9001):
+            nf = L // 4
+            sel = orc.select_blocks(rng.integers(-9, 9, nf).astype(np.float32), 512)
+            pages = -(-L // P)
+            ident = np.arange(pages)
+            p_c, n_c = orc.build_positions(sel, L, 0, 512)
+            p_i, n_i = orc.build_positions(sel, L, 0, 512, ident, P)
+            assert n_i == n_c and np.array_equal(p_i, p_c)
+            table = rng.permutation(pages + 7)[:pages]
+            p_p, n_p = orc.build_positions(sel, L, 0, 512, table, P)
+            assert n_p == n_c
+            logical = p_c[:n_c]
+            assert np.array_equal(p_p[:n_p], table[logical // P] * P + logical % P)
+            runs = p_p[:4 * min(nf, 512)].reshape(-1, 4)
+            assert np.all(np.diff(runs, axis=1) == 1)
+            assert np.all(p_p[n_p:] == -1)
+    w = make_custom("paged", [9000, 3001, 57], [4, 2, 1], 8, 2, seed=42)
+    ref = run_decode(orc, w, want_scores=False)
+    table, kc, vc = paged_layout(w, 16, 43)
+    got = orc.decode(w.q_start, w.seq_len, w.kv_start, w.blk_start, w.idx_q, w.ckeys, w.q, kc, vc,
+                     w.kv_dtype, w.k_scale, w.v_scale, want_scores=False, page_table=table, page_size=16)
+    assert np.array_equal(got["sel"], ref["sel"]) and np.array_equal(got["n_pos"], ref["n_pos"])
+    assert np.array_equal(got["out"], ref["out"])
+
+
+def check_positions_reuse(orc):
+    """A selection reused at a shorter length keeps exactly its blocks below
+    the new full-block count, then the new partial block."""
+    rng = np.random.default_rng(44)
+    L_sel = 20003
+    sel = orc.select_blocks(rng.integers(-50, 50, L_sel // 4).astype(np.float32), 512)
+    for L in (L_sel, L_sel - 1, L_sel - 3, 16000, 9, 4, 1):
+        nf = L // 4
+        keep = sel[sel < nf]
+        pos, n = orc.build_positions(sel, L, 100, 512)
+        assert n == 4 * keep.size + L % 4
+        want = np.concatenate([(100 + 4 * keep[:, None] + np.arange(4)).reshape(-1),
+                               100 + np.arange(4 * nf, L)])
+        assert np.array_equal(pos[:n], want) and np.all(pos[n:] == -1)
+
+
+def _nearest_bf16_bits(value: Fraction, all_neg_zero: bool) -> int:
+    """Brute force: among the BF16 patterns next to float32(value) pick the one
+    at the smallest exact distance, ties to the even pattern."""
+    if value == 0:
+        return 0x8000 if all_neg_zero else 0
+    f = np.float32(float(value)).view(np.uint32) >> 16
+    best = None
+    for cand in range(int(f) - 2, int(f) + 3):
+        c = cand & 0xFFFF
+        if (c & 0x7F80) == 0x7F80:
+            continue
+        cv = Fraction(float(np.array([c << 16], np.uint32).view(np.float32)[0]))
+        key = (abs(cv - value), c & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def check_compress_keys(orc):
+    """Block keys: the mean of the four token keys rounded once to BF16."""
+    bf = lambda x: bf16_bits_from_f32(np.asarray(x, np.float32))
+    one, e7, e6 = 1.0, 1.0 + 2 ** -7, 1.0 + 2 ** -6
+    cases = [
+        ([3, 5, 6, 2], 4.0),                    # exact mean
+        ([1, 2, 3, 5], 2.75),                   # exact quarter
+        ([one, one, one, e7], None),            # 1 + 2^-9: below half a unit -> 1
+        ([one, one, e7, e7], 1.0),              # 1 + 2^-8: tie -> even (1.0)
+        ([e6, e6, e7, e7], 1.0 + 2 ** -6),      # 1 + 3*2^-8: tie -> even (1 + 2^-6)
+    ]
+    for vals, want in cases:
+        got = orc.compress_block_key(bf(np.array(vals, np.float32))[:, None].repeat(3, 1))
+        if want is not None:
+            assert np.all(got == bf(np.float32(want))), (vals, got)
+    assert orc.compress_block_key(bf(np.array([one, one, one, e7], np.float32))[:, None])[0] == bf(np.float32(1.0))
+    # subnormal BF16 unit is 2^-133: mean of 2^-133 x {1, 1, 1, 0} = 0.75 units -> 1 unit
+    tiny = np.array([0x0001, 0x0001, 0x0001, 0x0000], np.uint16)[:, None]
+    assert orc.compress_block_key(tiny)[0] == 0x0001
+    # signed zeros: -0 only when all four are -0
+    z = np.array([0x8000, 0x8000, 0x8000, 0x8000], np.uint16)[:, None]
+    assert orc.compress_block_key(z)[0] == 0x8000
+    z[2, 0] = 0x0000
+    assert orc.compress_block_key(z)[0] == 0x0000
+    # brute-force nearest on random normals and wide magnitudes
+    rng = np.random.default_rng(45)
+    for scale in (1.0, 1e-38, 3e37):
+        x = (rng.standard_normal((4, 64)) * scale).astype(np.float32)
+        bits = bf(x)
+        got = orc.compress_block_key(bits)
+        vals = orc.bf16_to_f64(bits)
+        for dd in range(64):
+            m = sum(Fraction(float(v)) for v in vals[:, dd]) / 4
+            assert got[dd] == _nearest_bf16_bits(m, bool(np.all(bits[:, dd] == 0x8000))), (scale, dd)
+    # the blocks a step completes: prev_len <= 4b + 3 < seq_len
+    tok = bf(rng.standard_normal((40, 8)).astype(np.float32))
+    keys = orc.compress_new_keys(23, 6, tok, kv_start=3)
+    assert sorted(keys) == [1, 2, 3, 4]
+    assert np.array_equal(keys[2], orc.compress_block_key(tok[3 + 8:3 + 12]))
+    assert sorted(orc.compress_new_keys(8, 8, tok)) == [] and sorted(orc.compress_new_keys(9, 7, tok)) == [1]
+
+
 ALL_CHECKS = [
     check_fp8_decode, check_bf16_decode,
     check_scores_exact_integer, check_scores_unit_vectors, check_scores_rounded_once,
@@ -326,4 +435,5 @@ ALL_CHECKS = [
     check_select_signed_zero, check_select_tie_construction,
     check_positions_invariants, check_positions_mtp_lengths,
     check_attention_dense_equivalence, check_attention_over_selection, check_attention_special_cases,
+    check_paged_positions, check_positions_reuse, check_compress_keys,
 ]

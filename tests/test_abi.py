@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_the_five_stage_calls():
     names = declared_functions()
     for n in ("qsa_score", "qsa_select_topk", "qsa_build_index", "qsa_sparse_attn", "qsa_decode",
-              "qsa_workspace_bytes", "qsa_status_string", "qsa_abi_version"):
+              "qsa_workspace_bytes", "qsa_status_string", "qsa_abi_version", "qsa_compress_keys"):
         assert n in names
 
 
@@ -34,14 +34,14 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert qsa.abi_version() == 1
+    assert qsa.abi_version() == 2
     for s in range(6):
         assert qsa.status_string(s)
     assert qsa.status_string(99) == "unknown status"
 
 
-def _cbatch(num_req=1, num_q=4, max_blocks=12500, ptr=0x1000):
-    return qsa._CBatch(num_req, num_q, max_blocks, ptr, ptr, ptr, ptr)
+def _cbatch(num_req=1, num_q=4, max_blocks=12500, ptr=0x1000, page_table=None, page_size=0, pages=0):
+    return qsa._CBatch(num_req, num_q, max_blocks, ptr, ptr, ptr, ptr, page_table, page_size, pages)
 
 
 def test_workspace_bytes_host_only():
@@ -65,8 +65,17 @@ def test_error_paths_return_before_launch():
     assert lib.qsa_score(ctypes.byref(good), P, P, P, 100, None) == 2          # ld < max_blocks
     bad_q = _cbatch(num_req=1, num_q=5)
     assert lib.qsa_score(ctypes.byref(bad_q), P, P, P, 12500, None) == 2       # > 4 queries per request
-    nullmeta = qsa._CBatch(1, 1, 10, 0, 0, 0, 0)
+    nullmeta = qsa._CBatch(1, 1, 10, 0, 0, 0, 0, 0, 0, 0)
     assert lib.qsa_score(ctypes.byref(nullmeta), P, P, P, 10, None) == 1
+    # paged batches: page size a positive multiple of 4, at least one page per request;
+    # kv_start may then be NULL
+    assert lib.qsa_score(ctypes.byref(_cbatch(page_table=0x1000, page_size=6, pages=4)), P, P, P, 12500, None) == 2
+    assert lib.qsa_score(ctypes.byref(_cbatch(page_table=0x1000, page_size=16, pages=0)), P, P, P, 12500, None) == 2
+    assert lib.qsa_score(ctypes.byref(_cbatch(page_table=0x1000, page_size=0, pages=4)), P, P, P, 12500, None) == 2
+    nokv = qsa._CBatch(1, 4, 12500, 0x1000, 0x1000, 0, 0x1000, 0, 0, 0)
+    assert lib.qsa_build_index(ctypes.byref(nokv), P, P, 512, P, P, None) == 1
+    assert lib.qsa_compress_keys(ctypes.byref(good), None, P, P, None) == 1
+    assert lib.qsa_compress_keys(ctypes.byref(bad_q), P, P, P, None) == 2
     assert lib.qsa_select_topk(ctypes.byref(good), P, 12500, 0, P, P, None, 0, None) == 2
     assert lib.qsa_build_index(ctypes.byref(good), P, P, 600, P, P, None) == 2
     # attention: bad head geometry / dtype / scale / width / workspace

@@ -149,10 +149,71 @@ def _m_sel_pad_keeps_k(m):
     m.select_blocks = select_blocks
 
 
+def _m_page_no_scale(m):
+    orig = m.token_slots
+    def token_slots(t, kv_start=0, page_row=None, page_size=None):
+        if page_row is None:
+            return orig(t, kv_start)
+        t = np.asarray(t, dtype=np.int64)
+        return np.asarray(page_row, np.int64)[t // page_size] + t % page_size
+    m.token_slots = token_slots
+
+
+def _m_reuse_keeps_all(m):
+    def build_positions(sel, L, kv_start, k=m.TOPK, page_row=None, page_size=None):
+        sel = np.asarray(sel, dtype=np.int64)
+        nf = L // m.BLOCK
+        full = (m.BLOCK * sel[:, None] + np.arange(m.BLOCK)[None, :]).reshape(-1)
+        p = m.token_slots(np.concatenate([full, np.arange(m.BLOCK * nf, L)]), kv_start, page_row, page_size)
+        out = np.full(m.BLOCK * k + m.BLOCK - 1, -1, dtype=np.int64)
+        out[:p.shape[0]] = p
+        return out, int(p.shape[0])
+    m.build_positions = build_positions
+
+
+def _m_compress_truncate(m):
+    def bf16_bits_round_exact(value, negative_zero=False):
+        if value == 0:
+            return 0x8000 if negative_zero else 0
+        bits = int(np.array([float(value)], np.float32).view(np.uint32)[0])
+        return bits >> 16
+    m.bf16_bits_round_exact = bf16_bits_round_exact
+
+
+def _m_compress_ties_away(m):
+    F = m.Fraction
+    def bf16_bits_round_exact(value, negative_zero=False):
+        neg = value < 0
+        a = -value if neg else value
+        if a == 0:
+            return 0x8000 if negative_zero else 0
+        e = int(np.frexp(float(a))[1]) - 1
+        while F(2) ** e > a:
+            e -= 1
+        while F(2) ** (e + 1) <= a:
+            e += 1
+        unit = F(2) ** (max(e, -126) - 7)
+        n = a / unit
+        fl = n.numerator // n.denominator
+        if n - fl >= F(1, 2):                       # ties away from zero
+            fl += 1
+        bits = int(np.array([float(fl * unit)], np.float32).view(np.uint32)[0]) >> 16
+        return bits | (0x8000 if neg else 0)
+    m.bf16_bits_round_exact = bf16_bits_round_exact
+
+
+def _m_compress_first_block_off(m):
+    orig = m.compress_new_keys
+    def compress_new_keys(seq_len, prev_len, tok_keys, kv_start=0, page_row=None, page_size=None):
+        return orig(seq_len, min(int(prev_len) + 4, int(seq_len)), tok_keys, kv_start, page_row, page_size)
+    m.compress_new_keys = compress_new_keys
+
+
 MUTANTS = [_m_tie_higher_index, _m_unsorted_output, _m_bottom_k, _m_drop_partial, _m_no_kv_offset,
            _m_all_queries_full_length, _m_causal_off_by_one, _m_ignore_scale, _m_gqa_modulo,
            _m_fp8_bias8, _m_fp8_no_subnormals, _m_swap_kv_scales, _m_score_sign, _m_score_in_bf16,
-           _m_ignore_blk_start, _m_sel_pad_keeps_k]
+           _m_ignore_blk_start, _m_sel_pad_keeps_k, _m_page_no_scale, _m_reuse_keeps_all,
+           _m_compress_truncate, _m_compress_ties_away, _m_compress_first_block_off]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__[3:])

@@ -265,3 +265,26 @@ def make_workload(name: str) -> Workload:
         raise KeyError(name)
     return make_custom(name, lens, nq, hq, hkv, kv_dtype=cfg["kv"], seed=seed,
                        tie_fraction=tie, rng=rng)
+
+
+def paged_layout(w, page_size: int, seed: int):
+    """The workload's caches re-laid out in pages of page_size tokens placed at a
+    random permutation of physical pages, with the page table that maps them."""
+    rng = np.random.default_rng(seed)
+    seq = [int(x) for x in w.seq_len]
+    pages = [-(-s // page_size) for s in seq]
+    ppr = max(pages)
+    perm = rng.permutation(sum(pages))
+    table = np.zeros((len(seq), ppr), np.int64)
+    kc = np.zeros((sum(pages) * page_size,) + w.k_cache.shape[1:], w.k_cache.dtype)
+    vc = np.zeros_like(kc)
+    nxt = 0
+    for r, s in enumerate(seq):
+        for p in range(pages[r]):
+            phys = int(perm[nxt]); nxt += 1
+            table[r, p] = phys
+            lo, hi = p * page_size, min(s, (p + 1) * page_size)
+            src = int(w.kv_start[r]) + np.arange(lo, hi)
+            dst = phys * page_size + np.arange(hi - lo)
+            kc[dst], vc[dst] = w.k_cache[src], w.v_cache[src]
+    return table, kc, vc
