@@ -89,6 +89,7 @@ class Rig:
         self.pos = torch.empty((w.num_q, WIDTH), dtype=torch.int32, device="cuda")
         self.n_pos = torch.empty((w.num_q,), dtype=torch.int32, device="cuda")
         self.attn_ws = qsa.alloc_workspace(self.batch, hq, w.num_kv_heads)
+        self.sel_ws = qsa.alloc_workspace(self.batch, 1, 1)
 
     def decode(self, i):
         c = self.copies[i % len(self.copies)]
@@ -99,7 +100,7 @@ class Rig:
     def prepare_stage_inputs(self):
         c = self.copies[0]
         self.qsa.qsa_score(self.batch, c["idx_q"], c["ckeys"], self.scores)
-        self.qsa.qsa_select_topk(self.batch, self.scores, self.sel, self.n_sel)
+        self.qsa.qsa_select_topk(self.batch, self.scores, self.sel, self.n_sel, workspace=self.sel_ws)
         self.qsa.qsa_build_index(self.batch, self.sel, self.n_sel, self.pos, self.n_pos)
         self.torch.cuda.synchronize()
 
@@ -108,7 +109,7 @@ class Rig:
         if name == "score":
             self.qsa.qsa_score(self.batch, c["idx_q"], c["ckeys"], self.scores)
         elif name == "select":
-            self.qsa.qsa_select_topk(self.batch, self.scores, self.sel, self.n_sel)
+            self.qsa.qsa_select_topk(self.batch, self.scores, self.sel, self.n_sel, workspace=self.sel_ws)
         elif name == "attn":
             self.qsa.qsa_sparse_attn(self.batch, c["q"], c["k_cache"], c["v_cache"], self.pos, self.n_pos,
                                      self.outs[i % len(self.copies)], k_scale=c["k_scale"], v_scale=c["v_scale"],
@@ -165,7 +166,8 @@ def measure(name: str, steps: int, warmup: int, kernels: bool = True) -> dict:
     gbps = nbytes["step"] / (ms * 1e-3) / 1e9
     log(f"[{name}] qsa_decode: {ms * 1e3:.2f} us/step (graph, events), wall {wall_ms * 1e3:.2f} us/step, "
         f"{gbps:.0f} GB/s = {gbps / HBM_PEAK_GBPS:.1%} of HBM peak")
-    res = {"workload": name, "w": w, "copies": R, "ms_per_step": ms, "wall_ms_per_step": wall_ms,
+    res = {"workload": name, "w": w, "copies": R, "max_blocks": rig.batch.max_blocks,
+           "ms_per_step": ms, "wall_ms_per_step": wall_ms,
            "steps_per_s": 1e3 / ms, "step_bytes": nbytes["step"], "step_gbps": gbps, "kernels": {}}
     if kernels:
         rig.prepare_stage_inputs()
@@ -181,6 +183,9 @@ def measure(name: str, steps: int, warmup: int, kernels: bool = True) -> dict:
 
 
 KERNEL_NAMES = {"score": "qsa::score_kernel", "select": "qsa::select_reg_kernel", "attn": "qsa::attn_kernel"}
+# rows over 32,768 blocks take the five-kernel multi-workgroup top-k
+MS_SELECT_NAME = "qsa::ms_*_kernel (5 launches)"
+MS_MIN_BLOCKS = 32768
 CSRC = os.path.join(ROOT, "block_sparse_attention_qsa_amd", "csrc")
 
 
@@ -206,10 +211,13 @@ def roofline_of(res: dict, traffic: dict | None) -> dict:
     dom = max(ks, key=lambda s: ks[s]["us"])
     k = ks[dom]
     tr = None
-    key = f"{KERNEL_NAMES[dom]}@{res['workload']}"
+    name = KERNEL_NAMES[dom]
+    if dom == "select" and res.get("max_blocks", 0) > MS_MIN_BLOCKS:
+        name = MS_SELECT_NAME
+    key = f"{name}@{res['workload']}"
     if traffic and key in traffic.get("entries", {}) and traffic.get("source_sha256") == kernel_source_hash():
         tr = traffic["entries"][key]["bytes_per_launch"]
-    return {"kernel": KERNEL_NAMES[dom], "bound": "hbm", "achieved": round(k["gbps"], 1), "peak": HBM_PEAK_GBPS,
+    return {"kernel": name, "bound": "hbm", "achieved": round(k["gbps"], 1), "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": round(k["gbps"] / HBM_PEAK_GBPS, 4), "traffic": tr,
             "algorithmic_bytes_per_launch": k["bytes"], "avg_launch_us": round(k["us"], 3)}
 
@@ -258,6 +266,8 @@ def main():
     ap.add_argument("--config", default="mtp50k")
     ap.add_argument("--b32", default="mtp50k_b32_fp8", help="second workload reported beside (or 'none')")
     ap.add_argument("--b32-steps", type=int, default=200)
+    ap.add_argument("--long", default="mtp1m", help="long-context workload reported beside (or 'none')")
+    ap.add_argument("--long-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timings")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -310,6 +320,18 @@ def main():
                        "rotation_copies": r2["copies"]}
         if r2["kernels"]:
             line["b32"]["roofline"] = roofline_of(r2, traffic)
+    if args.long != "none":
+        r3 = measure(args.long, args.long_steps, min(args.warmup, 10), kernels=not args.no_kernels)
+        w3 = r3.pop("w")
+        line["long"] = {"workload": args.long, "steps_per_s": round(r3["steps_per_s"], 2),
+                        "ms_per_step": round(r3["ms_per_step"], 6), "step_gbps": round(r3["step_gbps"], 1),
+                        "step_frac_of_peak": round(r3["step_gbps"] / HBM_PEAK_GBPS, 4),
+                        "kernels_us": {k: round(v["us"], 3) for k, v in r3["kernels"].items()},
+                        "requests": w3.num_req, "queries": w3.num_q, "seq_len": int(w3.seq_len.max()),
+                        "kv_dtype": w3.kv_dtype, "rotation_copies": r3["copies"]}
+        if r3["kernels"]:
+            line["long"]["roofline"] = roofline_of(r3, traffic)
+        del w3
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
     print(json.dumps(line), flush=True)

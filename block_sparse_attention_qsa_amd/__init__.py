@@ -203,12 +203,16 @@ def qsa_score(batch: Batch, idx_q, ckeys, scores, stream=None) -> None:
 
 
 def qsa_select_topk(batch: Batch, scores, sel, n_sel, k: int = TOPK, workspace=None, stream=None) -> None:
+    """Rows longer than 32,768 blocks need workspace; without one, a
+    workspace of qsa_workspace_bytes() is allocated for the call."""
     _dev(scores, "scores", (torch.float32,))
     if scores.dim() != 2 or scores.shape[0] != batch.num_q:
         raise QsaError("scores must be [num_q, ld]")
     _dev(sel, "sel", (torch.int32,), (batch.num_q, k))
     _dev(n_sel, "n_sel", (torch.int32,), (batch.num_q,))
-    ws_n = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if workspace is None:
+        workspace = alloc_workspace(batch, 1, 1, k, device=scores.device)
+    ws_n = workspace.numel() * workspace.element_size()
     _check(lib().qsa_select_topk(batch.c, _ptr(scores), scores.shape[1], k, _ptr(sel), _ptr(n_sel),
                                  _ptr(workspace), ws_n, _stream(stream)), "qsa_select_topk")
 

@@ -15,7 +15,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct WsLayout {
-  size_t counters, partials, attn_end, scores, sel, n_sel, pos, n_pos, total;
+  size_t counters, partials, attn_end, scores, sel, n_sel, pos, n_pos, msel, total;
 };
 
 // Row stride of the workspace score buffer: a multiple of 4 floats so that
@@ -34,6 +34,7 @@ WsLayout ws_layout(int num_q, int max_blocks, int hq, int hkv, int k) {
   w.n_sel = off; off += align_up((size_t)num_q * sizeof(int32_t));
   w.pos = off; off += align_up((size_t)num_q * width * sizeof(int32_t));
   w.n_pos = off; off += align_up((size_t)num_q * sizeof(int32_t));
+  w.msel = off; off += align_up(qsa::select_workspace_bytes(num_q, max_blocks));
   w.total = off;
   return w;
 }
@@ -134,14 +135,14 @@ qsa_status qsa_score(const qsa_batch* batch, const void* idx_q, const void* ckey
 
 qsa_status qsa_select_topk(const qsa_batch* batch, const float* scores, int64_t ld, int32_t k, int32_t* sel,
                            int32_t* n_sel, void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   QSA_TRY(check_batch(batch));
   QSA_TRY(check_k(k));
   if (!scores || !sel || !n_sel) return QSA_ERR_NULL;
   if (ld < batch->max_blocks) return QSA_ERR_SHAPE;
+  const size_t need = qsa::select_workspace_bytes(batch->num_q, batch->max_blocks);
+  QSA_TRY(check_ws(ws, ws_bytes, need));
   return launched(qsa::launch_select(meta_of(batch), scores, ld, k, sel, n_sel, nullptr, nullptr,
-                                     QSA_BLOCK * k + QSA_BLOCK - 1, stream));
+                                     QSA_BLOCK * k + QSA_BLOCK - 1, ws, stream));
 }
 
 qsa_status qsa_build_index(const qsa_batch* batch, const int32_t* sel, const int32_t* n_sel, int32_t k,
@@ -218,7 +219,7 @@ qsa_status qsa_decode(const qsa_batch* batch, const void* idx_q, const void* cke
   const int64_t ld = score_ld(batch->max_blocks);
 
   QSA_TRY(launched(qsa::launch_score(m, idx_q, ckeys, scores, ld, stream)));
-  QSA_TRY(launched(qsa::launch_select(m, scores, ld, k, sel, n_sel, pos, n_pos, width, stream)));
+  QSA_TRY(launched(qsa::launch_select(m, scores, ld, k, sel, n_sel, pos, n_pos, width, base + w.msel, stream)));
   qsa::AttnArgs a;
   a.q = q;
   a.k_cache = k_cache;

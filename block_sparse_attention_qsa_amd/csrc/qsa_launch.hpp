@@ -46,9 +46,12 @@ struct AttnArgs {
 
 hipError_t launch_score(const Meta& m, const void* idx_q, const void* ckeys, float* scores, int64_t ld,
                         hipStream_t stream);
-// Writes sel/n_sel, and pos/n_pos too when pos != nullptr.
+// Writes sel/n_sel, and pos/n_pos too when pos != nullptr.  Rows longer than
+// 32,768 blocks use select_workspace_bytes() of workspace at ws (256-byte
+// aligned; no initial contents needed).
 hipError_t launch_select(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel,
-                         int32_t* n_sel, int32_t* pos, int32_t* n_pos, int width, hipStream_t stream);
+                         int32_t* n_sel, int32_t* pos, int32_t* n_pos, int width, void* ws, hipStream_t stream);
+size_t select_workspace_bytes(int num_q, int max_blocks);
 hipError_t launch_build_index(const Meta& m, const int32_t* sel, const int32_t* n_sel, int k, int32_t* pos,
                               int32_t* n_pos, int width, hipStream_t stream);
 hipError_t launch_attn(const Meta& m, const AttnArgs& a, hipStream_t stream);

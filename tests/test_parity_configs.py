@@ -1,4 +1,4 @@
-"""Fused qsa_decode against the oracle on the five named workloads at full
+"""Fused qsa_decode against the oracle on the named workloads at full
 size, in the launch configuration the benchmark times: selection and position
 buffers bit-exact for every query, FP32 output within 2e-3 * max|out|."""
 import gc
@@ -14,7 +14,7 @@ from gpu_helpers import assert_out_close, assert_selection_equal, need_gpu, orac
 
 pytestmark = pytest.mark.gpu
 
-CONFIG_NAMES = ["single8k", "mtp50k", "mtp50k_b32_fp8", "mtp262k_ties", "mtp262k_ties_fp8", "ragged64"]
+CONFIG_NAMES = ["single8k", "mtp50k", "mtp50k_b32_fp8", "mtp262k_ties", "mtp262k_ties_fp8", "ragged64", "mtp1m"]
 
 
 @pytest.mark.parametrize("name", CONFIG_NAMES)
@@ -35,7 +35,7 @@ def test_config_parity(name):
         for j in range(4):
             nf = (262144 - 4 + 1 + j) // 4
             assert np.array_equal(got["sel"][j], np.sort(tie[tie < nf])[:512])
-    if name == "mtp50k":
+    if name in ("mtp50k", "mtp1m"):
         assert list(got["n_pos"]) == [2049, 2050, 2051, 2048]
     # determinism: a second call gives identical bits
     again = run_decode(w, dev)
@@ -46,7 +46,7 @@ def test_config_parity(name):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("name", ["mtp50k", "mtp50k_b32_fp8", "ragged64"])
+@pytest.mark.parametrize("name", ["mtp50k", "mtp50k_b32_fp8", "ragged64", "mtp1m"])
 def test_scores_bit_exact_full_size(name):
     """Stage call a1 at full size (the batched workloads take the streaming
     score kernel): every FP32 score bit-identical, nothing written past a

@@ -100,6 +100,7 @@ SELECT_GROUPS = {
     "le32k": [3, 513, 4097, 16385, 20000, 32768],
     "le64k": [600, 32769, 40000, 65535, 65536],
     "stream": [700, 12500, 65537, 100000, 131072],
+    "ms262k": [5, 32769, 131073, 262144],
 }
 
 

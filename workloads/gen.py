@@ -238,6 +238,8 @@ CONFIGS = {
     "mtp262k_ties_fp8": dict(seed=104, heads=(32, 4), kv="fp8_e4m3"),
     # 64 requests, lengths log-uniform in [1, 131072], 1 or 4 queries each, 16 / 2 heads
     "ragged64": dict(seed=105, heads=(16, 2), kv="bf16"),
+    # one request, 4 verify queries, a 1,048,576-token context (262,144 blocks), 32 / 4 heads, BF16
+    "mtp1m": dict(seed=106, heads=(32, 4), kv="bf16"),
 }
 
 
@@ -256,6 +258,8 @@ def make_workload(name: str) -> Workload:
         lens, nq = (50000 + 800 * t).tolist(), [4] * 32
     elif name.startswith("mtp262k_ties"):
         lens, nq, tie = [262144], [4], 0.05
+    elif name == "mtp1m":
+        lens, nq = [1 << 20], [4]
     elif name == "ragged64":
         u = rng.random(64)
         lens = np.clip(np.floor(np.exp(u * math.log(131072.0))), 1, 131072).astype(np.int64)
