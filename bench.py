@@ -235,6 +235,113 @@ def calibrate_copy(gib: int = 1, reps: int = 3) -> None:
     torch.cuda.empty_cache()
 
 
+# ------------------------------------------------------------------ profile summaries
+PROFILE_WORKLOADS = ("mtp50k", "mtp50k_b32_fp8", "mtp1m")
+PROF_STATS_CMD = ("rocprofv3 --kernel-trace --stats -d {d}/stats_{W} -o qsa --output-format csv -- "
+                  "python -u bench.py --config {W} --b32 none --long none --steps 200 --warmup 20 --cpu-seconds 0")
+PROF_PMC_CMD = ("rocprofv3 --pmc {C} --kernel-trace -d {d}/pmc_{C}_{W} -o qsa --output-format csv -- "
+                "python -u bench.py --config {W} --b32 none --long none --steps 10 --warmup 2 --cpu-seconds 0 "
+                "--no-kernels --calibrate-copy")
+
+
+def _stage_of(kernel: str):
+    if "attn_kernel" in kernel:
+        return "attn"
+    if "score_kernel" in kernel:
+        return "score"
+    if "select_reg_kernel" in kernel or "qsa::ms_" in kernel:
+        return "select"
+    return None
+
+
+def summarize_profiles(prof_dir: str, out_dir: str) -> None:
+    """Turn the rocprofv3 CSV output of PROF_STATS_CMD and PROF_PMC_CMD (one
+    directory per workload and counter under prof_dir) into one markdown
+    summary per workload and traffic.json under out_dir.  The memory counters
+    are scaled by what they read for the 1 GiB device copy of --calibrate-copy;
+    the five launches of the multi-workgroup top-k are summed into one entry."""
+    import collections
+    import csv
+    from workloads import make_workload
+
+    def rows(path):
+        with open(path) as f:
+            return list(csv.DictReader(f))
+
+    traffic = {"source_sha256": kernel_source_hash(), "entries": {}}
+    for W in PROFILE_WORKLOADS:
+        stats_csv = os.path.join(prof_dir, f"stats_{W}", "qsa_kernel_stats.csv")
+        if not os.path.exists(stats_csv):
+            log(f"[summarize] no profile for {W}")
+            continue
+        pmc = {}
+        for C in ("FETCH_SIZE", "WRITE_SIZE"):
+            agg = collections.defaultdict(list)
+            for r in rows(os.path.join(prof_dir, f"pmc_{C}_{W}", "qsa_counter_collection.csv")):
+                agg[r["Kernel_Name"].split("(")[0]].append(float(r["Counter_Value"]))
+            pmc[C] = agg
+        copy = "__amd_rocclr_copyBuffer"
+        cf, cw = 1048576.0 / max(pmc["FETCH_SIZE"][copy]), 1048576.0 / max(pmc["WRITE_SIZE"][copy])
+        alg = algorithmic_bytes(make_workload(W))
+        line = {}
+        log_path = os.path.join(prof_dir, f"stats_{W}.log")
+        if os.path.exists(log_path):
+            with open(log_path) as f:
+                js = [l for l in f if l.startswith("{")]
+            line = json.loads(js[-1]) if js else {}
+        fmt = dict(d=prof_dir, W=W)
+        out = [f"# rocprofv3 summary: QSA kernels on `{W}`", "",
+               f"MI355X (gfx950), one GPU.  Library sources sha256 `{traffic['source_sha256'][:16]}`.", "",
+               "## Kernel trace statistics", "", "```", PROF_STATS_CMD.format(**fmt), "```", "",
+               "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
+        for r in rows(stats_csv):
+            n = r["Name"].split("(")[0]
+            if "qsa::" in n or "copyBuffer" in n:
+                out.append(f"| `{n}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                           f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | "
+                           f"{float(r['Percentage']):.2f} |")
+        if line:
+            out += ["", f"bench.py in the same run (HIP events around graph replays): step "
+                        f"{line['ms_per_step'] * 1e3:.2f} us, per kernel {line.get('kernels_us')} us."]
+        out += ["", "## HBM traffic (memory counters, fused qsa_decode only)", "", "```",
+                PROF_PMC_CMD.format(C="FETCH_SIZE", **fmt), PROF_PMC_CMD.format(C="WRITE_SIZE", **fmt),
+                f"python bench.py --summarize-profiles {prof_dir}", "```", "",
+                f"Calibration: a 1 GiB device copy reads FETCH_SIZE {max(pmc['FETCH_SIZE'][copy]):.1f} KiB and "
+                f"WRITE_SIZE {max(pmc['WRITE_SIZE'][copy]):.1f} KiB per dispatch: scale factors {cf:.4f} (FETCH) "
+                f"and {cw:.4f} (WRITE).", "",
+                "| kernel | dispatches | FETCH KiB | WRITE KiB | scaled HBM MB / launch | algorithmic MB / launch "
+                "| ratio |", "|---|---|---|---|---|---|---|"]
+        summed = collections.defaultdict(lambda: [0.0, 0.0, 0.0])
+        for n in sorted(pmc["FETCH_SIZE"]):
+            st = _stage_of(n)
+            if st is None:
+                continue
+            fv, wv = pmc["FETCH_SIZE"][n], pmc["WRITE_SIZE"].get(n, [0.0])
+            fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+            tot = (fk * cf + wk * cw) * 1024
+            out.append(f"| `{n}` | {len(fv)} | {fk:.1f} | {wk:.1f} | {tot / 1e6:.3f} | "
+                       f"{alg[st] / 1e6 if 'qsa::ms_' not in n else float('nan'):.3f} | "
+                       f"{tot / alg[st] if 'qsa::ms_' not in n else float('nan'):.3f} |")
+            key = MS_SELECT_NAME if "qsa::ms_" in n else KERNEL_NAMES[st]
+            acc = summed[key]
+            acc[0] += fk
+            acc[1] += wk
+            acc[2] += tot
+        for key, (fk, wk, tot) in summed.items():
+            st = [s for s in KERNEL_NAMES if KERNEL_NAMES[s] == key or (key == MS_SELECT_NAME and s == "select")][0]
+            if key == MS_SELECT_NAME:
+                out.append(f"| {key}, summed | | {fk:.1f} | {wk:.1f} | {tot / 1e6:.3f} | {alg[st] / 1e6:.3f} | "
+                           f"{tot / alg[st]:.3f} |")
+            traffic["entries"][f"{key}@{W}"] = {"bytes_per_launch": int(round(tot)), "fetch_kib": fk,
+                                                "write_kib": wk, "fetch_scale": cf, "write_scale": cw,
+                                                "algorithmic_bytes": alg[st]}
+        with open(os.path.join(out_dir, f"qsa_kernels__{W}.md"), "w") as f:
+            f.write("\n".join(out) + "\n")
+        log(f"[summarize] {W}: wrote qsa_kernels__{W}.md")
+    with open(os.path.join(out_dir, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+
+
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(name: str, seconds: float) -> dict:
     import oracle
@@ -274,7 +381,12 @@ def main():
                     help="HBM traffic per launch measured by rocprofv3 counters")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a 1 GiB device copy (reference for memory-counter scaling)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="no GPU: summarize rocprofv3 output under DIR into profiles/ and exit")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, os.path.join(ROOT, "profiles"))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (run with --gpus 1)",
               file=sys.stderr)
