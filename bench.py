@@ -189,16 +189,27 @@ MS_MIN_BLOCKS = 32768
 CSRC = os.path.join(ROOT, "block_sparse_attention_qsa_amd", "csrc")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over every HIP source and header of the library (sorted by name)."""
+def _code_text(src: bytes) -> bytes:
+    """Source text without // comments, trailing blanks and empty lines: edits
+    to comments leave the hash (and the counters tied to it) valid."""
+    import re
+    lines = (re.sub(rb"//.*$", b"", l).rstrip() for l in src.splitlines())
+    return b"\n".join(l for l in lines if l)
+
+
+def kernel_source_hash(read=None) -> str:
+    """sha256 over the code of every HIP source and header of the library
+    (sorted by name) and the public header, comments stripped."""
     import hashlib
+    if read is None:
+        def read(rel):
+            with open(os.path.join(ROOT, rel), "rb") as f:
+                return f.read()
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
         if name.endswith((".hip", ".hpp", ".h")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
-    with open(os.path.join(ROOT, "include", "qsa.h"), "rb") as f:
-        h.update(f.read())
+            h.update(name.encode() + b"\0" + _code_text(read(f"block_sparse_attention_qsa_amd/csrc/{name}")))
+    h.update(_code_text(read("include/qsa.h")))
     return h.hexdigest()
 
 
@@ -291,7 +302,7 @@ def summarize_profiles(prof_dir: str, out_dir: str) -> None:
             line = json.loads(js[-1]) if js else {}
         fmt = dict(d=prof_dir, W=W)
         out = [f"# rocprofv3 summary: QSA kernels on `{W}`", "",
-               f"MI355X (gfx950), one GPU.  Library sources sha256 `{traffic['source_sha256'][:16]}`.", "",
+               f"MI355X (gfx950), one GPU.  Library code sha256 (comments stripped) `{traffic['source_sha256'][:16]}`.", "",
                "## Kernel trace statistics", "", "```", PROF_STATS_CMD.format(**fmt), "```", "",
                "| kernel | calls | avg us | min us | max us | % of GPU time |", "|---|---|---|---|---|---|"]
         for r in rows(stats_csv):

@@ -7,20 +7,20 @@
 // article (first optimisation) adds the last step: locate the kept pieces in
 // the KV cache.
 //
-// One 1024-thread workgroup handles one query.  Rows of up to 65,536 blocks
-// are held in registers (contiguous segment per thread); longer rows use a
-// streaming variant that stages only the threshold bin's keys in LDS.
-//   1. FP32 scores -> order-preserving uint32 keys (-0.0 folded onto +0.0),
-//      staged in LDS when they fit.
-//   2. Three MSB-first radix passes (11, 11, 10 bits) with LDS histograms find
-//      the key T of the k-th best block and how many blocks equal to T to keep.
-//   3. An ordered compaction (one packed block scan over contiguous
-//      per-thread segments) keeps every key > T and the lowest-index keys == T,
-//      so ties go to the lower block index and the output is ascending.
-// Scans are DPP shift-scans inside each 16-lane row; the bucket search after a
-// histogram pass is done by a single wave.  When the keys do not fit in LDS,
-// the first pass streams the score buffer and only the keys falling in the
-// chosen top-level bin are staged for the remaining passes.
+// Three selectors, chosen by the longest row of the batch:
+//   * rows of up to 32,768 blocks: select_reg_kernel, one workgroup per query
+//     with the whole row in registers (a linear value grid finds the bin of
+//     the k-th best score, its few candidates are ranked exactly);
+//   * longer rows: five multi-workgroup launches over 4,096-block slices that
+//     share the same value grid, with per-query state in caller workspace;
+//   * any row the grid cannot split (no finite range, NaN scores, a crowded
+//     threshold bin) falls back to exact MSB-first radix passes over
+//     order-preserving keys: in registers inside select_reg_kernel, streamed
+//     from the score buffer by select_stream_row behind the multi-workgroup
+//     launches.
+// All three keep every block above the threshold and the lowest-index blocks
+// that tie with it, and write sel (and, fused, pos) in ascending order.
+
 #include "qsa_common.hpp"
 #include "qsa_launch.hpp"
 
@@ -30,7 +30,7 @@ constexpr int kKeyCap = 32768;   // keys staged in LDS (128 KiB of the 160 KiB a
 constexpr int kBatch = 8;        // loads a thread keeps in flight while streaming scores
 constexpr int kCandCap = 256;    // threshold-bin population ranked directly
 
-// Inside the fully unrolled per-element loops: a scheduling fence every 8
+// Inside the fully unrolled per-element loops: a scheduling fence every 4
 // elements, so the compiler does not compute all E derived values before
 // consuming them (with 64 keys per thread in registers that spills).
 __device__ __forceinline__ void sched_fence(int e) {
