@@ -88,10 +88,21 @@ __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_fl
 template <bool kFp8> struct VRaw { typedef u32x4 type; };   // 8 BF16 of one V row
 template <> struct VRaw<true> { typedef u32x2 type; };      // 8 FP8 of one V row
 
+// First of the 8 dimensions that step kk of the S = K Q^T chain contracts in
+// lane group kg.  A K load instruction w reads bytes 64w + 16kg .. 64w + 16kg
+// + 15 of each of its 16 rows, so the four lane groups read 64 contiguous
+// bytes of a row together.  BF16: load w holds dimensions 32w + 8kg .. + 7,
+// step kk = w.  FP8: load w holds dimensions 64w + 16kg .. + 15, the first
+// half for step 2w, the second for step 2w + 1.  The query uses the same map.
+template <bool kFp8>
+__device__ __forceinline__ int kdim(int kk, int kg) {
+  return kFp8 ? 64 * (kk >> 1) + 16 * kg + 8 * (kk & 1) : 32 * kk + 8 * kg;
+}
+
 // Raw K/V bytes of one 32-position chunk as one lane holds them.
 template <bool kFp8>
 struct ChunkRaw {
-  u32x4 k[2][kFp8 ? 2 : 4];             // K rows 16t + j: dims kg*32 .. kg*32+31
+  u32x4 k[2][kFp8 ? 2 : 4];             // K rows 16t + j: 16 bytes at 64w + 16kg (see kdim)
   typename VRaw<kFp8>::type v[8];       // V rows 16t + 4kg + rr (e = 4t + rr): dims 8j .. 8j+7
   uint32_t vmask;                       // bit e: V / score position e holds a valid slot
 };
@@ -125,7 +136,7 @@ __device__ __forceinline__ void issue_chunk(ChunkRaw<kFp8>& ch, const ChunkHeads
                                             const uint8_t* kbase, const uint8_t* vbase, uint32_t row_stride, int j,
                                             int kg) {
   constexpr int EB = kFp8 ? 1 : 2;
-  const uint8_t* kl = kbase + kg * 32 * EB;   // this lane's bytes inside a K row
+  const uint8_t* kl = kbase + 16 * kg;        // this lane's bytes inside a K row: 64w + 16kg
   const uint8_t* vl = vbase + j * 8 * EB;     // and inside a V row
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -133,7 +144,7 @@ __device__ __forceinline__ void issue_chunk(ChunkRaw<kFp8>& ch, const ChunkHeads
     const uint32_t slot = (uint32_t)(i < npos ? h.k[t] + (j & 3) : slot0);
     const uint8_t* kr = kl + (uint64_t)slot * row_stride;
 #pragma unroll
-    for (int w = 0; w < (kFp8 ? 2 : 4); ++w) ch.k[t][w] = *reinterpret_cast<const u32x4*>(kr + 16 * w);
+    for (int w = 0; w < (kFp8 ? 2 : 4); ++w) ch.k[t][w] = *reinterpret_cast<const u32x4*>(kr + 64 * w);
   }
   uint32_t vm = 0;
 #pragma unroll
@@ -151,7 +162,7 @@ __device__ __forceinline__ void issue_chunk(ChunkRaw<kFp8>& ch, const ChunkHeads
 template <bool kFp8>
 __device__ __forceinline__ void compute_chunk(const ChunkRaw<kFp8>& ch, const bf16x8 (&qb)[4], float sl2,
                                               float& m_run, float& l_run, f32x4 (&o)[8]) {
-  // K operand (A): lane holds dims kg*32 .. kg*32+31 of its row, as 4 x 8 bf16.
+  // K operand (A): step kk takes the 8 dimensions kdim(kk, kg) of the lane's row.
   bf16x8 ka[2][4];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -275,10 +286,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   const int slot0 = prow[0];
   bf16x8 qb[4];
   {
-    const uint16_t* qrow = p.q + ((int64_t)q * Hq + g * G + j) * D + kg * 32;
+    const uint16_t* qrow = p.q + ((int64_t)q * Hq + g * G + j) * D;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      u32x4 v = hvalid ? *reinterpret_cast<const u32x4*>(qrow + kk * 8) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 v = hvalid ? *reinterpret_cast<const u32x4*>(qrow + kdim<kFp8>(kk, kg)) : u32x4{0u, 0u, 0u, 0u};
       qb[kk] = __builtin_bit_cast(bf16x8, v);
     }
   }

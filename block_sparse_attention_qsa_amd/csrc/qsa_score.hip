@@ -3,83 +3,127 @@
 //
 // The arex-research.com article (section on the four optimisations, item 2)
 // describes the MTP-verify reuse this kernel is built around: up to 4 queries
-// of one request share a single load of each compressed-key tile.  Here a
-// wave reads 4 key rows (1 KiB, 16 lanes x 16 B per row, fully coalesced) per
-// load instruction and scores every row against all of the request's queries
-// from registers, so each key byte crosses HBM once per request.  The
-// contraction is 4 queries x 128: far too thin for MFMA, so it runs on the
-// packed BF16 dot-product VALU op with FP32 accumulation and a DPP reduction
-// across the 16 lanes of a row.
+// of one request share a single load of each compressed-key tile, so each key
+// byte crosses HBM once per request.
+//
+// The contraction of a 16-row key tile with the request's queries is one
+// bf16 MFMA 16x16x32 chain (4 steps over the 128 dimensions): the key rows
+// are the M side, the queries the N side (4 of 16 columns used - the matrix
+// core still does it in a fraction of the issue time of packed dot products
+// plus a cross-lane reduction).  Products of two BF16 values are exact and
+// accumulate in FP32.
+//
+// Step kk of the chain contracts dimensions 32kk .. 32kk+31: lane l = 16g + n
+// of a wave loads bytes 64kk + 16g .. 64kk + 16g + 15 of key row n of a
+// 16-row group, so one load instruction reads 64 contiguous bytes of each of
+// 16 rows and the two instructions of a 128-byte line follow each other.  The
+// result leaves lane (g, n) with query n's scores of rows 4g .. 4g+3, stored
+// as one 16-byte vector.
+//
+// Each wave takes tiles of 16U rows.  Up to 16,384 workgroups a wave has one
+// tile (measured fastest on MI355X from 50K-token batches to 1M-token rows);
+// on larger batches waves loop over several tiles, with the next tile's loads
+// issued before the current one is contracted.
 #include "qsa_common.hpp"
 #include "qsa_launch.hpp"
 
 namespace qsa {
 
-// ROWS_PER_WAVE rows per wave, 4 waves per workgroup.
-template <int ITERS>
+constexpr int kScoreWaves = 4;             // waves per workgroup
+constexpr int kKeyPolicy = 0;              // buffer-load cache policy of the key stream
+constexpr int kRowBytes = QSA_INDEX_DIM * 2;
+
+template <int U>
+struct KeyTile {
+  u32x4 w[U][4];    // group u, step kk: dimensions 32kk + 8g .. 32kk + 8g + 7 of row 16u + n
+};
+
+template <int U>
+__device__ __forceinline__ void load_tile(KeyTile<U>& t, __amdgpu_buffer_rsrc_t rs, int row0, int n, int g) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int off = (row0 + 16 * u + n) * kRowBytes + 16 * g;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      t.w[u][kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * kk, 0,
+                                                                                    kKeyPolicy));
+  }
+}
+
+// Contract one tile and store the scores of rows below nblk (one 16-byte
+// store per lane when the score rows are 16-byte aligned).
+template <int U>
+__device__ __forceinline__ void score_tile(const KeyTile<U>& t, const bf16x8 (&qb)[4], float* qrow, bool qvalid,
+                                           bool vec, int row0, int nblk, int g) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.w[u][kk]), qb[kk], acc, 0, 0, 0);
+    const int row = row0 + 16 * u + 4 * g;
+    if (qvalid) {
+      if (vec && row + 3 < nblk) {
+        *reinterpret_cast<f32x4*>(qrow + row) = acc;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (row + i < nblk) qrow[row + i] = acc[i];
+      }
+    }
+  }
+}
+
+// Grid (x, request).  Wave w of workgroup x takes tiles x*4 + w, then every
+// gridDim.x * 4 tiles after it, of its request's rows.
+template <int U>
 __global__ __launch_bounds__(256) void score_kernel(Meta m, const uint16_t* __restrict__ idx_q,
                                                     const uint16_t* __restrict__ ckeys,
-                                                    float* __restrict__ scores, int64_t ld) {
-  constexpr int kRowsPerWg = 16 * ITERS;
+                                                    float* __restrict__ scores, int64_t ld, int vec) {
+  constexpr int R = 16 * U;
   const int r = blockIdx.y;
   int nblk = m.seq_len[r] >> 2;
   if (nblk > m.max_blocks) nblk = m.max_blocks;
-  const int row0 = blockIdx.x * kRowsPerWg;
-  if (row0 >= nblk) return;
+  const int ntiles = (nblk + R - 1) / R;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int stride = gridDim.x * kScoreWaves;
+  int tile = blockIdx.x * kScoreWaves + wave;
+  if (tile >= ntiles) return;                 // no barriers below: waves leave on their own
+  const int n = lane & 15, g = lane >> 4;
+
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(ckeys) + (int64_t)m.blk_start[r] * QSA_INDEX_DIM, 0, nblk * kRowBytes, 0x00020000);
+  KeyTile<U> a, b;
+  load_tile<U>(a, rs, tile * R, n, g);
+
   const int qs = m.q_start[r];
   const int nq = m.q_start[r + 1] - qs;
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
-  const int sub = lane & 15;      // 8 dims per lane: sub*8 .. sub*8+7
-  const int rsub = lane >> 4;     // row within a group of 4
-
-  u32x4 iq[QSA_MAX_Q_PER_REQ];
+  const bool qvalid = n < nq;
+  bf16x8 qb[4];
+  {
+    const uint16_t* qp = idx_q + (int64_t)(qs + (qvalid ? n : 0)) * QSA_INDEX_DIM + 8 * g;
 #pragma unroll
-  for (int qi = 0; qi < QSA_MAX_Q_PER_REQ; ++qi) {
-    if (qi < nq)
-      iq[qi] = *reinterpret_cast<const u32x4*>(idx_q + (int64_t)(qs + qi) * QSA_INDEX_DIM + sub * 8);
-    else
-      iq[qi] = u32x4{0u, 0u, 0u, 0u};
+    for (int kk = 0; kk < 4; ++kk)
+      qb[kk] = __builtin_bit_cast(bf16x8, qvalid ? *reinterpret_cast<const u32x4*>(qp + 32 * kk)
+                                                 : u32x4{0u, 0u, 0u, 0u});
   }
+  float* qrow = scores + (int64_t)(qs + (qvalid ? n : 0)) * ld;
 
-  const uint16_t* kbase = ckeys + (int64_t)m.blk_start[r] * QSA_INDEX_DIM + sub * 8;
-  u32x4 kr[ITERS];
-#pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    const int row = row0 + it * 16 + wave * 4 + rsub;
-    if (row < nblk)
-      kr[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + (int64_t)row * QSA_INDEX_DIM));
-    else
-      kr[it] = u32x4{0u, 0u, 0u, 0u};
-  }
-
-  // Lane sub = 4Q + x of a 16-lane row ends with query Q's score for that
-  // row: a butterfly over the row sums the four queries' partial dot
-  // products at once (exchange with lane ^ 8, then with the mirrored lane of
-  // the 8-lane half, then inside the quad), 5 DPP adds instead of 4 x 4.
-  const bool hi8 = (sub & 8) != 0, hi4 = (sub & 4) != 0;
-  const int qsel = sub >> 2;
-#pragma unroll
-  for (int it = 0; it < ITERS; ++it) {
-    const int row = row0 + it * 16 + wave * 4 + rsub;
-    float a[QSA_MAX_Q_PER_REQ];
-#pragma unroll
-    for (int qi = 0; qi < QSA_MAX_Q_PER_REQ; ++qi) {
-      float acc = 0.f;
-      acc = fdot2_bf16(kr[it].x, iq[qi].x, acc);
-      acc = fdot2_bf16(kr[it].y, iq[qi].y, acc);
-      acc = fdot2_bf16(kr[it].z, iq[qi].z, acc);
-      acc = fdot2_bf16(kr[it].w, iq[qi].w, acc);
-      a[qi] = acc;
-    }
-    const float k0 = hi8 ? a[2] : a[0], k1 = hi8 ? a[3] : a[1];
-    const float s0 = hi8 ? a[0] : a[2], s1 = hi8 ? a[1] : a[3];
-    const float b0 = k0 + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s0), 0x128, 0xF, 0xF, false));
-    const float b1 = k1 + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(s1), 0x128, 0xF, 0xF, false));
-    const float kk = hi4 ? b1 : b0, ss = hi4 ? b0 : b1;
-    float c = kk + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x141, 0xF, 0xF, false));
-    c += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(c), 0x4E, 0xF, 0xF, false));
-    c += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(c), 0xB1, 0xF, 0xF, false));
-    if ((sub & 3) == 0 && qsel < nq && row < nblk) scores[(int64_t)(qs + qsel) * ld + row] = c;
+  // Ping-pong over two register tiles: the loads of the next tile are in
+  // flight while the current one is contracted.
+  for (;;) {
+    int next = tile + stride;
+    if (next < ntiles) load_tile<U>(b, rs, next * R, n, g);
+    __builtin_amdgcn_sched_barrier(0);
+    score_tile<U>(a, qb, qrow, qvalid, vec != 0, tile * R, nblk, g);
+    if (next >= ntiles) break;
+    tile = next;
+    next = tile + stride;
+    if (next < ntiles) load_tile<U>(a, rs, next * R, n, g);
+    __builtin_amdgcn_sched_barrier(0);
+    score_tile<U>(b, qb, qrow, qvalid, vec != 0, tile * R, nblk, g);
+    if (next >= ntiles) break;
+    tile = next;
   }
 }
 
@@ -87,19 +131,16 @@ hipError_t launch_score(const Meta& m, const void* idx_q, const void* ckeys, flo
                         hipStream_t stream) {
   const int64_t mb = m.max_blocks;
   if (mb == 0) return hipSuccess;
-  auto wgs = [&](int rows) { return ((mb + rows - 1) / rows) * (int64_t)m.num_req; };
-  const uint16_t* iq = static_cast<const uint16_t*>(idx_q);
-  const uint16_t* ck = static_cast<const uint16_t*>(ckeys);
-  if (wgs(64) >= 1024) {
-    dim3 grid((unsigned)((mb + 63) / 64), (unsigned)m.num_req);
-    score_kernel<4><<<grid, 256, 0, stream>>>(m, iq, ck, scores, ld);
-  } else if (wgs(32) >= 1024) {
-    dim3 grid((unsigned)((mb + 31) / 32), (unsigned)m.num_req);
-    score_kernel<2><<<grid, 256, 0, stream>>>(m, iq, ck, scores, ld);
-  } else {
-    dim3 grid((unsigned)((mb + 15) / 16), (unsigned)m.num_req);
-    score_kernel<1><<<grid, 256, 0, stream>>>(m, iq, ck, scores, ld);
-  }
+  constexpr int U = 1;
+  constexpr int kTargetWgs = 16384;           // beyond this, waves loop over several tiles
+  const int64_t tiles = (mb + 16 * U - 1) / (16 * U);
+  int64_t gx = (tiles + kScoreWaves - 1) / kScoreWaves;
+  const int64_t cap = (kTargetWgs + m.num_req - 1) / m.num_req;
+  if (gx > cap) gx = cap;
+  const dim3 grid((unsigned)gx, (unsigned)m.num_req);
+  const int vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
+  score_kernel<U><<<grid, 256, 0, stream>>>(m, static_cast<const uint16_t*>(idx_q),
+                                            static_cast<const uint16_t*>(ckeys), scores, ld, vec);
   return hipGetLastError();
 }
 
