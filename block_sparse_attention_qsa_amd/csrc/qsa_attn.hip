@@ -35,21 +35,20 @@
 namespace qsa {
 
 constexpr int kOStride = QSA_HEAD_DIM + 4;   // padded LDS row of one head's output
-// Device-scope (sc1) 16-byte loads and stores through a raw buffer descriptor
-// of a split-partial region: they bypass the per-XCD caches, so workgroups on
-// different XCDs see each other's partials without any cache flush.
-constexpr int kCpolSc1 = 16;                 // cache-policy bit SC1 (device scope)
+// Device-scope 16-byte loads and stores through a raw buffer descriptor of a
+// split-partial region.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(float* base) {
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, 0x7fffffff, 0x00020000);
 }
 __device__ __forceinline__ f32x4 load_coherent(__amdgpu_buffer_rsrc_t r, int float_off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, float_off * 4, 0, kCpolSc1);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, float_off * 4, 0, kCpolDevice);
 }
 __device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, int float_off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, float_off * 4, 0, kCpolSc1);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, float_off * 4, 0, kCpolDevice);
 }
 constexpr int kMaxHeads = 8 * ((QSA_WIDTH + kChunk - 1) / kChunk);   // block heads of one split
 constexpr float kRescaleSlack = 8.f;     // log2 headroom of the softmax reference maximum
+constexpr int kNtMinUnits = 256;         // (query, KV head) units from which K/V loads are non-temporal
 
 struct AttnParams {
   const uint16_t* q;
@@ -128,10 +127,17 @@ __device__ __forceinline__ ChunkHeads lds_heads(const int* heads_s, int c_rel, i
   return h;
 }
 
+// Load of one K/V piece; kNt marks it non-temporal (streamed past the caches).
+template <bool kNt, class T>
+__device__ __forceinline__ T kv_load(const uint8_t* p) {
+  if constexpr (kNt) return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  else return *reinterpret_cast<const T*>(p);
+}
+
 // Issue the K/V loads of the chunk starting at position `base`.  Positions at
 // or past `npos` (all of them when the chunk is past the end) read the first
 // slot instead and are masked out, so the issue never needs a branch.
-template <bool kFp8>
+template <bool kFp8, bool kNt>
 __device__ __forceinline__ void issue_chunk(ChunkRaw<kFp8>& ch, const ChunkHeads& h, int base, int npos, int slot0,
                                             const uint8_t* kbase, const uint8_t* vbase, uint32_t row_stride, int j,
                                             int kg) {
@@ -144,7 +150,7 @@ __device__ __forceinline__ void issue_chunk(ChunkRaw<kFp8>& ch, const ChunkHeads
     const uint32_t slot = (uint32_t)(i < npos ? h.k[t] + (j & 3) : slot0);
     const uint8_t* kr = kl + (uint64_t)slot * row_stride;
 #pragma unroll
-    for (int w = 0; w < (kFp8 ? 2 : 4); ++w) ch.k[t][w] = *reinterpret_cast<const u32x4*>(kr + 64 * w);
+    for (int w = 0; w < (kFp8 ? 2 : 4); ++w) ch.k[t][w] = kv_load<kNt, u32x4>(kr + 64 * w);
   }
   uint32_t vm = 0;
 #pragma unroll
@@ -154,7 +160,7 @@ __device__ __forceinline__ void issue_chunk(ChunkRaw<kFp8>& ch, const ChunkHeads
     const bool valid = i < npos;
     vm |= (uint32_t)valid << e;
     const uint32_t slot = (uint32_t)(valid ? h.v[t] + rr : slot0);
-    ch.v[e] = *reinterpret_cast<const typename VRaw<kFp8>::type*>(vl + (uint64_t)slot * row_stride);
+    ch.v[e] = kv_load<kNt, typename VRaw<kFp8>::type>(vl + (uint64_t)slot * row_stride);
   }
   ch.vmask = vm;
 }
@@ -250,13 +256,12 @@ __device__ __forceinline__ void compute_chunk(const ChunkRaw<kFp8>& ch, const bf
   }
 }
 
-template <bool kFp8, bool kOutBf16>
+template <bool kFp8, bool kOutBf16, bool kNt>
 __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   constexpr int D = QSA_HEAD_DIM;
   constexpr int EB = kFp8 ? 1 : 2;            // bytes per KV element
   __shared__ float o_s[kAttnWaves][16][kOStride];
   __shared__ float m_s[kAttnWaves][16], l_s[kAttnWaves][16];
-  __shared__ float w_s[16];
   __shared__ float ml_s[kMaxSplits][32];
   __shared__ int heads_s[kMaxHeads];
   __shared__ int s_last;
@@ -316,19 +321,19 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
     // its compute (which would serialise load latency and math again).
     ChunkRaw<kFp8> ca, cb;
     const int nl = cfirst < c_end ? npos : 0;
-    issue_chunk<kFp8>(ca, lds_heads(heads_s, cfirst - c0, p.cps, j, kg), cfirst * kChunk, nl, slot0, kbase, vbase,
+    issue_chunk<kFp8, kNt>(ca, lds_heads(heads_s, cfirst - c0, p.cps, j, kg), cfirst * kChunk, nl, slot0, kbase, vbase,
                       row_stride, j, kg);
     __builtin_amdgcn_sched_barrier(0);
     for (int c = cfirst; c < c_end; c += 2 * kAttnWaves) {
       const int cn = c + kAttnWaves;
-      issue_chunk<kFp8>(cb, lds_heads(heads_s, cn - c0, p.cps, j, kg), cn * kChunk, cn < c_end ? npos : 0, slot0,
+      issue_chunk<kFp8, kNt>(cb, lds_heads(heads_s, cn - c0, p.cps, j, kg), cn * kChunk, cn < c_end ? npos : 0, slot0,
                         kbase, vbase, row_stride, j, kg);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk<kFp8>(ca, qb, sl2, m_run, l_run, o);
       __builtin_amdgcn_sched_barrier(0);
       if (cn >= c_end) break;
       const int cnn = cn + kAttnWaves;
-      issue_chunk<kFp8>(ca, lds_heads(heads_s, cnn - c0, p.cps, j, kg), cnn * kChunk, cnn < c_end ? npos : 0,
+      issue_chunk<kFp8, kNt>(ca, lds_heads(heads_s, cnn - c0, p.cps, j, kg), cnn * kChunk, cnn < c_end ? npos : 0,
                         slot0, kbase, vbase, row_stride, j, kg);
       __builtin_amdgcn_sched_barrier(0);
       compute_chunk<kFp8>(cb, qb, sl2, m_run, l_run, o);
@@ -337,7 +342,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   } else {
     for (int c = cfirst; c < c_end; c += kAttnWaves) {
       ChunkRaw<kFp8> cur;
-      issue_chunk<kFp8>(cur, lds_heads(heads_s, c - c0, p.cps, j, kg), c * kChunk, npos, slot0, kbase, vbase,
+      issue_chunk<kFp8, kNt>(cur, lds_heads(heads_s, c - c0, p.cps, j, kg), c * kChunk, npos, slot0, kbase, vbase,
                         row_stride, j, kg);
       compute_chunk<kFp8>(cur, qb, sl2, m_run, l_run, o);
     }
@@ -436,12 +441,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
 
   // Last workgroup of the unit: 16-byte device-scope loads bring every
   // split's maxima, sums and numerators (one round for groups of <= 8 heads).
+  // Each thread then weighs the splits of its own head from LDS itself (the
+  // 2*S reads are independent, so they overlap), with no further barrier.
   const int S = p.splits;
   if (tid < S * 8) {
     const int t = tid / 8, r4 = tid % 8;
     *reinterpret_cast<f32x4*>(&ml_s[t][4 * r4]) = load_coherent(unit_rs, t * pstride + nout + 4 * r4);
   }
-  // Rounds of one 4-output vector per thread (one round for groups of <= 8 heads).
   for (int v0 = 0; v0 < nout / 4; v0 += blockDim.x) {
     const int v4 = v0 + tid;
     f32x4 vals[kMaxSplits];
@@ -449,29 +455,26 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
     for (int t = 0; t < kMaxSplits; ++t)
       vals[t] = (t < S && v4 < nout / 4) ? load_coherent(unit_rs, t * pstride + 4 * v4)
                                          : f32x4{0.f, 0.f, 0.f, 0.f};
-    if (v0 == 0) {
-      __syncthreads();
-      if (tid < G) {
-        float M = -INFINITY;
-        for (int t = 0; t < S; ++t) M = fmaxf(M, ml_s[t][tid]);
-        float den = 0.f;
-        for (int t = 0; t < S; ++t) {
-          const float mt = ml_s[t][tid];
-          const float wgt = mt == -INFINITY ? 0.f : exp2f(mt - M);
-          ml_s[t][tid] = wgt;                       // weight of split t for head tid
-          den += wgt * ml_s[t][16 + tid];
-        }
-        w_s[tid] = vscale / den;
-      }
-      __syncthreads();
-    }
+    if (v0 == 0) __syncthreads();
     if (v4 < nout / 4) {
       const int hh = (4 * v4) / D;
-      f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+      float mt[kMaxSplits], M = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < kMaxSplits; ++t)
-        if (t < S) num += ml_s[t][hh] * vals[t];
-      num *= w_s[hh];
+      for (int t = 0; t < kMaxSplits; ++t) {
+        mt[t] = t < S ? ml_s[t][hh] : -INFINITY;
+        M = fmaxf(M, mt[t]);
+      }
+      f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+      float den = 0.f;
+#pragma unroll
+      for (int t = 0; t < kMaxSplits; ++t) {
+        if (t < S) {
+          const float wgt = mt[t] == -INFINITY ? 0.f : exp2f(mt[t] - M);
+          den += wgt * ml_s[t][16 + hh];
+          num += wgt * vals[t];
+        }
+      }
+      num *= vscale / den;
       const int64_t oi = ((int64_t)q * Hq + g * G) * D + 4 * v4;
       if (kOutBf16) {
         __bf16* op = static_cast<__bf16*>(p.out) + oi;
@@ -514,13 +517,23 @@ hipError_t launch_attn(const Meta& m, const AttnArgs& a, hipStream_t stream) {
   p.splits = sp.splits;
   p.cps = sp.chunks_per_split;
   const dim3 grid((unsigned)((int64_t)m.num_q * sp.splits * a.num_kv_heads));
+  // Large batches stream K/V with non-temporal loads (measured faster once
+  // the (query, KV head) units alone fill the chip); small ones keep the
+  // default policy (faster there).
+  const bool nt = (int64_t)m.num_q * a.num_kv_heads >= kNtMinUnits;
+#define QSA_ATTN_LAUNCH(F8, OB)                                              \
+  do {                                                                        \
+    if (nt) attn_kernel<F8, OB, true><<<grid, 256, 0, stream>>>(p);           \
+    else attn_kernel<F8, OB, false><<<grid, 256, 0, stream>>>(p);             \
+  } while (0)
   if (a.kv_fp8) {
-    if (a.out_bf16) attn_kernel<true, true><<<grid, 256, 0, stream>>>(p);
-    else attn_kernel<true, false><<<grid, 256, 0, stream>>>(p);
+    if (a.out_bf16) QSA_ATTN_LAUNCH(true, true);
+    else QSA_ATTN_LAUNCH(true, false);
   } else {
-    if (a.out_bf16) attn_kernel<false, true><<<grid, 256, 0, stream>>>(p);
-    else attn_kernel<false, false><<<grid, 256, 0, stream>>>(p);
+    if (a.out_bf16) QSA_ATTN_LAUNCH(false, true);
+    else QSA_ATTN_LAUNCH(false, false);
   }
+#undef QSA_ATTN_LAUNCH
   return hipGetLastError();
 }
 

@@ -21,6 +21,10 @@ constexpr int kSelectThreads = 1024;   // threads of one top-k workgroup
 constexpr int kRadixBins = 2048;       // 11-bit digits: passes over bits 31..21, 20..10, 9..0
 constexpr int kMaxSplits = (QSA_WIDTH + kChunk * kAttnWaves - 1) / (kChunk * kAttnWaves);  // 17
 constexpr int kCounterStride = 32;     // uint32 words per arrival counter (one 128-byte line)
+// Cache-policy bit SC1 of a buffer load/store: device scope.  Such accesses
+// bypass the per-XCD caches, so workgroups on different XCDs see each
+// other's data without any cache flush or invalidation.
+constexpr int kCpolDevice = 16;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 

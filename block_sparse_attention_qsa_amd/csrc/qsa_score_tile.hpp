@@ -1,0 +1,58 @@
+// a1 building block shared by the scoring kernels: the block scores of one
+// 16-row compressed-key tile against up to 4 index queries on one bf16 MFMA
+// 16x16x32 chain.
+//
+// The arex-research.com article (section on the four optimisations, item 2)
+// lets up to 4 verify queries of a request share one load of each
+// compressed-key tile; here the key rows are the M side of the MFMA and the
+// queries the N side (4 of 16 columns used).  Products of two BF16 values are
+// exact and accumulate in FP32.
+//
+// Step kk of the chain contracts dimensions 32kk .. 32kk+31: lane l = 16g + n
+// of a wave loads bytes 64kk + 16g .. 64kk + 16g + 15 of key row n of the
+// tile, so one load instruction reads 64 contiguous bytes of each of 16 rows.
+// The result leaves lane (g, n) with query n's scores of rows 4g .. 4g+3.
+#pragma once
+
+#include "qsa_common.hpp"
+
+namespace qsa {
+
+constexpr int kKeyRowBytes = QSA_INDEX_DIM * 2;
+
+struct KeyTile {
+  u32x4 w[4];    // step kk: dimensions 32kk + 8g .. 32kk + 8g + 7 of row n
+};
+
+// Loads of the tile starting at key row row0 of the rows behind rs (reads
+// past the descriptor's bound return zeros).
+__device__ __forceinline__ void load_key_tile(KeyTile& t, __amdgpu_buffer_rsrc_t rs, int row0, int n, int g) {
+  const int off = (row0 + n) * kKeyRowBytes + 16 * g;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    t.w[kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * kk, 0, 0));
+}
+
+// The request's index queries as the MFMA B operand: lane (g, n) holds query
+// n's dimensions 32kk + 8g .. + 7 for step kk (zeros for n >= nq).
+__device__ __forceinline__ void load_index_queries(bf16x8 (&qb)[4], const uint16_t* idx_q, int qs, int nq, int n,
+                                                   int g) {
+  const bool valid = n < nq;
+  // The load always reads a real row (query qs for the unused columns) and is
+  // masked afterwards: no branch, so all four loads issue back to back.
+  const uint16_t* qp = idx_q + (int64_t)(qs + (valid ? n : 0)) * QSA_INDEX_DIM + 8 * g;
+  const uint32_t keep = valid ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    qb[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qp + 32 * kk) & keep);
+}
+
+__device__ __forceinline__ f32x4 contract_key_tile(const KeyTile& t, const bf16x8 (&qb)[4]) {
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.w[kk]), qb[kk], acc, 0, 0, 0);
+  return acc;
+}
+
+}  // namespace qsa

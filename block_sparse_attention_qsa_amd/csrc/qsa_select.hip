@@ -170,11 +170,12 @@ __device__ __forceinline__ float wave_min_f32(float v) {
 //      pos.
 // The per-element work of the common path is a bin, two compares and a
 // ballot; only the few candidates take branches.
+// The selector body for query q, run by a whole NT-thread workgroup.
 template <int E, int NT, bool kWritePos>
-__global__ __launch_bounds__(NT) void select_reg_kernel(Meta m, const float* __restrict__ scores, int64_t ld,
-                                                        int k, int32_t* __restrict__ sel,
-                                                        int32_t* __restrict__ n_sel, int32_t* __restrict__ pos,
-                                                        int32_t* __restrict__ n_pos, int width) {
+__device__ __forceinline__ void select_row(const Meta& m, const float* __restrict__ scores, int64_t ld, int k,
+                                           int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
+                                           int32_t* __restrict__ pos, int32_t* __restrict__ n_pos, int width,
+                                           const int q) {
   constexpr int NW = NT / kWave;
   constexpr int ER = E > 32 ? 32 : E;    // scores per thread held in registers
   constexpr int EL = E - ER;             // the rest sit in LDS, column-major
@@ -194,7 +195,6 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(Meta m, const float* __r
   __shared__ int32_t sel_s[QSA_TOPK];
   __shared__ uint32_t s_prefix, s_krem, s_count, s_total, s_ncand;
 
-  const int q = blockIdx.x;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   const float* srow = scores + (int64_t)q * ld;
 
@@ -212,7 +212,8 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(Meta m, const float* __r
   if ((ld & 3) == 0) {
 #pragma unroll
     for (int v = 0; v < E / 4; ++v) {
-      const f32x4 x = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (beg + 4 * v) * 4, 0, 0));
+      const f32x4 x =
+          __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (beg + 4 * v) * 4, 0, 0));
       sv[4 * v] = x.x;
       sv[4 * v + 1] = x.y;
       sv[4 * v + 2] = x.z;
@@ -520,6 +521,14 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(Meta m, const float* __r
   }
 }
 #undef QSA_X
+
+template <int E, int NT, bool kWritePos>
+__global__ __launch_bounds__(NT) void select_reg_kernel(Meta m, const float* __restrict__ scores, int64_t ld,
+                                                        int k, int32_t* __restrict__ sel,
+                                                        int32_t* __restrict__ n_sel, int32_t* __restrict__ pos,
+                                                        int32_t* __restrict__ n_pos, int width) {
+  select_row<E, NT, kWritePos>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, (int)blockIdx.x);
+}
 
 // Exact selection of one query's row by a whole 1024-thread workgroup (any
 // row length, any scores): the body of select_stream_kernel, also the
