@@ -296,12 +296,22 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   // ---- 2. grid histogram, then classification
   int B0 = 0, h = 0;
   uint32_t krem = (uint32_t)k, c0 = (uint32_t)nf;
+  // Segments of up to 32 elements keep each element's grid bin from the
+  // histogram pass (bin + 1, 0 for none; two per word), so classifying needs
+  // no second bin computation.
+  constexpr bool kKeepBins = E <= 32;
+  uint32_t bins[kKeepBins ? E / 2 : 1];
   if (grid) {
     const float lo0 = fresh_uniform(lo), inv0 = fresh_uniform(inv);
     if (wave_full) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        atomicAdd(&hist[0][grid_bin(QSA_X(e), lo0, inv0)], 1u);
+        const int b = grid_bin(QSA_X(e), lo0, inv0);
+        atomicAdd(&hist[0][b], 1u);
+        if (kKeepBins) {
+          if (e & 1) bins[e >> 1] |= (uint32_t)(b + 1) << 16;
+          else bins[e >> 1] = (uint32_t)(b + 1);
+        }
         sched_fence(e);
       }
     } else if (!wave_empty) {
@@ -309,6 +319,10 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
       for (int e = 0; e < E; ++e) {
         const int b = grid_bin(QSA_X(e), lo0, inv0);
         if (b >= 0) atomicAdd(&hist[0][b], 1u);
+        if (kKeepBins) {
+          if (e & 1) bins[e >> 1] |= (uint32_t)(b + 1) << 16;
+          else bins[e >> 1] = (uint32_t)(b + 1);
+        }
         sched_fence(e);
       }
     }
@@ -331,28 +345,38 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   inb.clear();
   if (grid) {
     if (!wave_empty) {
-      const float lo1 = fresh_uniform(lo), inv1 = fresh_uniform(inv);
+      if (kKeepBins) {
+        const uint32_t b1 = (uint32_t)B0 + 1u;
 #pragma unroll
-      for (int e = E - 1; e >= 0; --e) {
-        const float x = QSA_X(e);
-        const int b = grid_bin(x, lo1, inv1);
-        above.push(e, b > B0);
-        inb.push(e, b == B0);
-        if (kFuseStage && ranked) {
-          // stage the candidate (wave-aggregated append)
-          const bool mine = b == B0;
-          const uint64_t bal = __ballot(mine);
-          if (bal) {
-            uint32_t wbase = 0;
-            if (lane == __builtin_ctzll(bal)) wbase = atomicAdd(&s_ncand, (uint32_t)__popcll(bal));
-            wbase = (uint32_t)__builtin_amdgcn_readlane((int)wbase, __builtin_ctzll(bal));
-            const uint32_t slot =
-                __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            if (mine && wbase + slot < (uint32_t)kCandCap)
-              cand_s[wbase + slot] = u32x2{score_key(x), (uint32_t)(beg + e)};
+        for (int e = E - 1; e >= 0; --e) {
+          const uint32_t b = (bins[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          above.push(e, b > b1);
+          inb.push(e, b == b1);
+        }
+      } else {
+        const float lo1 = fresh_uniform(lo), inv1 = fresh_uniform(inv);
+#pragma unroll
+        for (int e = E - 1; e >= 0; --e) {
+          const int b = grid_bin(QSA_X(e), lo1, inv1);
+          above.push(e, b > B0);
+          inb.push(e, b == B0);
+          sched_fence(e);
+        }
+      }
+      if (kFuseStage && ranked) {
+        // Stage this thread's candidates (few in a row, so most waves skip
+        // this): one LDS append per thread that has any.
+        const uint32_t mine = inb.count();
+        if (__ballot(mine != 0u)) {
+          uint32_t slot = mine != 0u ? atomicAdd(&s_ncand, mine) : 0u;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            if (inb.test(e)) {
+              if (slot < (uint32_t)kCandCap) cand_s[slot] = u32x2{score_key(QSA_X(e)), (uint32_t)(beg + e)};
+              ++slot;
+            }
           }
         }
-        sched_fence(e);
       }
     }
   } else {
