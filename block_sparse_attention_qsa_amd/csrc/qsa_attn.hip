@@ -5,7 +5,7 @@
 // BF16 queries and BF16 or FP8 E4M3 KV.  This is a gfx950 design for the same
 // contract.
 //
-// Work unit: (query, split of the position buffer, KV head), query fastest in
+// Work unit: (query, KV head, split of the position buffer), query fastest in
 // the 1-D grid.  A wave takes
 // 32 gathered positions per step and serves the whole GQA group of that KV
 // head (up to 16 query heads) at once on bf16 MFMA 16x16x32:
@@ -266,12 +266,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   __shared__ int heads_s[kMaxHeads];
   __shared__ int s_last;
 
-  // 1-D grid, query fastest, then split, then KV head.
+  // 1-D grid, query fastest, then KV head, then split: the last split of
+  // every unit, which holds only the few positions past the last full
+  // 4-chunk group, is dispatched last, so when the grid has more workgroups
+  // than the chip has CUs it is those nearly empty workgroups that share a
+  // CU with another.
   const int Hkv = p.num_kv_heads;
   const int num_q = (int)(gridDim.x / (unsigned)(Hkv * p.splits));
   const int q = blockIdx.x % num_q;
-  const int s = (blockIdx.x / num_q) % p.splits;
-  const int g = blockIdx.x / (num_q * p.splits);
+  const int g = (blockIdx.x / num_q) % Hkv;
+  const int s = blockIdx.x / (num_q * Hkv);
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int j = lane & 15, kg = lane >> 4;
   const int G = p.group;
