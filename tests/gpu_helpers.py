@@ -37,7 +37,7 @@ def oracle_decode(w, **kw):
                          w.k_cache, w.v_cache, w.kv_dtype, w.k_scale, w.v_scale, sm_scale=SM_SCALE, **kw)
 
 
-def run_decode(w, dev=None, out_dtype=torch.float32, k=qsa.TOPK):
+def run_decode(w, dev=None, out_dtype=torch.float32, k=qsa.TOPK, ws=None):
     dev = upload(w) if dev is None else dev
     b = batch_of(w)
     hq = w.num_q_heads
@@ -47,7 +47,7 @@ def run_decode(w, dev=None, out_dtype=torch.float32, k=qsa.TOPK):
     n_sel = torch.full((w.num_q,), -7, dtype=torch.int32, device="cuda")
     pos = torch.full((w.num_q, width), -7, dtype=torch.int32, device="cuda")
     n_pos = torch.full((w.num_q,), -7, dtype=torch.int32, device="cuda")
-    ws = qsa.alloc_workspace(b, hq, w.num_kv_heads, k)
+    ws = qsa.alloc_workspace(b, hq, w.num_kv_heads, k) if ws is None else ws
     qsa.qsa_decode(b, dev["idx_q"], dev["ckeys"], dev["q"], dev["k_cache"], dev["v_cache"], out, ws,
                    k_scale=dev["k_scale"], v_scale=dev["v_scale"], k=k, sm_scale=SM_SCALE,
                    sel=sel, n_sel=n_sel, pos=pos, n_pos=n_pos)

@@ -253,6 +253,9 @@ def test_decode_deterministic_and_workspace_reusable():
     say("qsa_decode determinism", w.name)
     dev = upload(w)
     a = run_decode(w, dev)
-    b = run_decode(w, dev)
-    assert np.array_equal(a["out"].view(np.uint64), b["out"].view(np.uint64))
-    assert np.array_equal(a["pos"], b["pos"])
+    # one workspace serves consecutive calls (each call leaves it reusable)
+    b = run_decode(w, dev, ws=a["ws"])
+    c = run_decode(w, dev, ws=a["ws"])
+    for x in (b, c):
+        assert np.array_equal(a["out"].view(np.uint64), x["out"].view(np.uint64))
+        assert np.array_equal(a["pos"], x["pos"])
