@@ -10,8 +10,7 @@
 // bf16 MFMA chain (qsa_score_tile.hpp).  Each wave takes 16-row tiles; up to
 // 16,384 workgroups a wave has one tile (measured fastest on MI355X from
 // 50K-token batches to 1M-token rows); on larger batches waves loop over
-// several tiles, with the next tile's loads issued before the current one is
-// contracted.
+// several tiles.
 #include "qsa_launch.hpp"
 #include "qsa_score_tile.hpp"
 
@@ -32,10 +31,14 @@ __device__ __forceinline__ void store_scores(float* qrow, f32x4 acc, bool vec, i
 }
 
 // Grid (x, request).  Wave w of workgroup x takes tiles x*4 + w, then every
-// gridDim.x * 4 tiles after it, of its request's rows.
+// gridDim.x * 4 tiles after it, of its request's rows.  A wave's tile goes
+// to its own 4 KiB of LDS (direct-to-LDS loads, whole lines, non-temporal),
+// is read back into MFMA operands, and the next tile's loads are issued
+// into the same LDS before the current tile is contracted.
 __global__ __launch_bounds__(256) void score_kernel(Meta m, const uint16_t* __restrict__ idx_q,
                                                     const uint16_t* __restrict__ ckeys,
                                                     float* __restrict__ scores, int64_t ld, int vec) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile_s[kScoreWaves][kTileBytes];
   const int r = blockIdx.y;
   // All of the request's metadata is read at once (one scalar round trip
   // after the kernel arguments), before anything depends on it.
@@ -49,11 +52,11 @@ __global__ __launch_bounds__(256) void score_kernel(Meta m, const uint16_t* __re
   int tile = blockIdx.x * kScoreWaves + wave;
   if (tile >= ntiles) return;                 // no barriers below: waves leave on their own
   const int n = lane & 15, g = lane >> 4;
+  uint8_t* my_tile = tile_s[wave];
 
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(ckeys) + (int64_t)row0 * QSA_INDEX_DIM, 0, nblk * kKeyRowBytes, 0x00020000);
-  KeyTile a, b;
-  load_key_tile(a, rs, tile * 16, n, g);
+  load_key_tile_lds(my_tile, rs, tile * 16, lane);
   __builtin_amdgcn_sched_barrier(0);          // key loads before the query loads
 
   const int nq = qe - qs;
@@ -62,21 +65,18 @@ __global__ __launch_bounds__(256) void score_kernel(Meta m, const uint16_t* __re
   load_index_queries(qb, idx_q, qs, nq, n, g);
   float* qrow = scores + (int64_t)(qs + (qvalid ? n : 0)) * ld;
 
-  // Ping-pong over two register tiles: the loads of the next tile are in
-  // flight while the current one is contracted.
   for (;;) {
-    int next = tile + stride;
-    if (next < ntiles) load_key_tile(b, rs, next * 16, n, g);
+    __builtin_amdgcn_s_waitcnt(0);            // this wave's tile (and the queries) have landed
+    KeyTile t;
+    read_key_tile_lds(t, my_tile, n, g);
+    const int next = tile + stride;
+    if (next < ntiles) {
+      __builtin_amdgcn_s_waitcnt(0);          // LDS reads done before the buffer is refilled
+      load_key_tile_lds(my_tile, rs, next * 16, lane);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    const f32x4 sa = contract_key_tile(a, qb);
-    if (qvalid) store_scores(qrow, sa, vec != 0, tile * 16 + 4 * g, nblk);
-    if (next >= ntiles) break;
-    tile = next;
-    next = tile + stride;
-    if (next < ntiles) load_key_tile(a, rs, next * 16, n, g);
-    __builtin_amdgcn_sched_barrier(0);
-    const f32x4 sb = contract_key_tile(b, qb);
-    if (qvalid) store_scores(qrow, sb, vec != 0, tile * 16 + 4 * g, nblk);
+    const f32x4 sc = contract_key_tile(t, qb);
+    if (qvalid) store_scores(qrow, sc, vec != 0, tile * 16 + 4 * g, nblk);
     if (next >= ntiles) break;
     tile = next;
   }
