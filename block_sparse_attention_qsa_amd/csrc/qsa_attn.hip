@@ -98,32 +98,86 @@ __device__ __forceinline__ int kdim(int kk, int kg) {
   return kFp8 ? 64 * (kk >> 1) + 16 * kg + 8 * (kk & 1) : 32 * kk + 8 * kg;
 }
 
-// Raw K/V bytes of one 32-position chunk as one lane holds them.
-template <bool kFp8>
+// K/V bytes of one 32-position chunk as one lane holds them.  With kKL the
+// chunk's K rows go to LDS instead (see KLds) and k is unused.
+template <bool kFp8, bool kKL>
 struct ChunkRaw {
-  u32x4 k[2][kFp8 ? 2 : 4];             // K rows 16t + j: 16 bytes at 64w + 16kg (see kdim)
+  u32x4 k[kKL ? 1 : 2][kFp8 ? 2 : 4];   // K rows 16t + j: 16 bytes at 64w + 16kg (see kdim)
   typename VRaw<kFp8>::type v[8];       // V rows 16t + 4kg + rr (e = 4t + rr): dims 8j .. 8j+7
   uint32_t vmask;                       // bit e: V / score position e holds a valid slot
+};
+
+// K rows of a chunk in LDS: 32 rows of 128 (FP8) or 256 (BF16) bytes, row
+// r's 16-byte piece p stored at slot p XOR kswz(r).  Direct-to-LDS loads
+// put lane l's 16 bytes at byte 16l of the instruction's 1 KiB, so an
+// instruction moves 8 (FP8) or 4 (BF16) whole rows and each aligned group of
+// 8 lanes fetches one whole 128-byte line; the swizzle then makes the MFMA
+// operand reads (16 rows, one piece each) hit 16 different bank groups.
+// LDS reads issued as inline assembly that waits for its own results.  The
+// compiler treats any LDS read that follows a direct-to-LDS load as possibly
+// reading that load's data and waits for every vector-memory operation in
+// flight, which would drain the next chunk's prefetch; the reads here touch
+// only LDS the loads in flight do not write (block heads, or a K buffer whose
+// loads were waited for explicitly).
+__device__ __forceinline__ void lds_read_2x_b128(u32x4& a, u32x4& b, const uint8_t* pa, const uint8_t* pb) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(a), "=&v"(b)
+               : "v"((__attribute__((address_space(3))) const uint8_t*)pa),
+                 "v"((__attribute__((address_space(3))) const uint8_t*)pb));
+}
+
+template <bool kFp8> struct KLds {
+  static constexpr int kRowBytes = kFp8 ? 128 : 256;
+  static constexpr int kBytes = 32 * kRowBytes;              // one chunk
+  static constexpr int kLoads = kBytes / 1024;               // load instructions per chunk
+  static constexpr int kBufs = kFp8 ? 2 : 1;                 // FP8 double-buffers chunks
+  __device__ static constexpr int swz(int r) { return kFp8 ? (r >> 1) & 7 : r & 15; }
 };
 
 // Block heads of one chunk: the position buffer is made of runs of 4
 // consecutive slots (one 4-token block each), so entry i is head(i & ~3) + (i & 3).
 struct ChunkHeads {
-  int k[2];   // heads of the blocks holding K rows 16t + j
+  int k[8];   // heads of the blocks holding K rows 16t + j (registers), or the K rows this lane moves to LDS (load i)
   int v[2];   // heads of the blocks holding V rows 16t + 4kg + rr
 };
 
 // Block heads of chunk c from the workgroup's LDS copy (heads_s[8 * (c - c0) + b]
 // is the slot of position 32c + 4b).  LDS reads do not join the in-order
 // vector-memory counter, so they never force a wait on K/V loads in flight.
-__device__ __forceinline__ ChunkHeads lds_heads(const int* heads_s, int c_rel, int cps, int j, int kg) {
-  ChunkHeads h;
+template <bool kFp8, bool kKL>
+__device__ __forceinline__ ChunkHeads lds_heads(const int* heads_s, int c_rel, int cps, int lane, int j, int kg) {
+  constexpr int kRowsPerLoad = 1024 / KLds<kFp8>::kRowBytes;
+  constexpr int kLanesPerRow = KLds<kFp8>::kRowBytes / 16;
   c_rel = min(c_rel, cps - 1);          // chunks past the split only issue masked loads
+  if (!kKL) {
+    ChunkHeads h;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    h.k[t] = heads_s[8 * c_rel + 4 * t + (j >> 2)];
-    h.v[t] = heads_s[8 * c_rel + 4 * t + kg];
+    for (int t = 0; t < 2; ++t) {
+      h.k[t] = heads_s[8 * c_rel + 4 * t + (j >> 2)];
+      h.v[t] = heads_s[8 * c_rel + 4 * t + kg];
+    }
+    return h;
   }
+  u32x4 a, b;                           // the chunk's 8 block heads
+  lds_read_2x_b128(a, b, reinterpret_cast<const uint8_t*>(heads_s + 8 * c_rel),
+                   reinterpret_cast<const uint8_t*>(heads_s + 8 * c_rel + 4));
+  ChunkHeads h;
+  const bool odd = lane >> 5;
+  // block of K row kRowsPerLoad * i + lane / kLanesPerRow: FP8 loads cover
+  // blocks 2i, 2i+1 (lane halves), BF16 loads one block each
+  if (kRowsPerLoad == 8) {
+    h.k[0] = (int)(odd ? a.y : a.x);
+    h.k[1] = (int)(odd ? a.w : a.z);
+    h.k[2] = (int)(odd ? b.y : b.x);
+    h.k[3] = (int)(odd ? b.w : b.z);
+  } else {
+    h.k[0] = (int)a.x; h.k[1] = (int)a.y; h.k[2] = (int)a.z; h.k[3] = (int)a.w;
+    h.k[4] = (int)b.x; h.k[5] = (int)b.y; h.k[6] = (int)b.z; h.k[7] = (int)b.w;
+  }
+  // V rows 16t + 4kg + rr sit in block 4t + kg
+  h.v[0] = (int)((kg & 2) ? ((kg & 1) ? a.w : a.z) : ((kg & 1) ? a.y : a.x));
+  h.v[1] = (int)((kg & 2) ? ((kg & 1) ? b.w : b.z) : ((kg & 1) ? b.y : b.x));
+  (void)kLanesPerRow;
   return h;
 }
 
@@ -137,21 +191,35 @@ __device__ __forceinline__ T kv_load(const uint8_t* p) {
 // Issue the K/V loads of the chunk starting at position `base`.  Positions at
 // or past `npos` (all of them when the chunk is past the end) read the first
 // slot instead and are masked out, so the issue never needs a branch.
-template <bool kFp8, bool kNt>
-__device__ __forceinline__ void issue_chunk(ChunkRaw<kFp8>& ch, const ChunkHeads& h, int base, int npos, int slot0,
-                                            const uint8_t* kbase, const uint8_t* vbase, uint32_t row_stride, int j,
-                                            int kg) {
+template <bool kFp8, bool kNt, bool kKL>
+__device__ __forceinline__ void issue_chunk(ChunkRaw<kFp8, kKL>& ch, uint8_t* klds, const ChunkHeads& h, int base,
+                                            int npos, int slot0, const uint8_t* kbase, const uint8_t* vbase,
+                                            uint32_t row_stride, int lane, int j, int kg) {
   constexpr int EB = kFp8 ? 1 : 2;
-  const uint8_t* kl = kbase + 16 * kg;        // this lane's bytes inside a K row: 64w + 16kg
-  const uint8_t* vl = vbase + j * 8 * EB;     // and inside a V row
+  constexpr int kRowsPerLoad = 1024 / KLds<kFp8>::kRowBytes;
+  constexpr int kLanesPerRow = KLds<kFp8>::kRowBytes / 16;
+  if (kKL) {
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int i = base + 16 * t + j;
-    const uint32_t slot = (uint32_t)(i < npos ? h.k[t] + (j & 3) : slot0);
-    const uint8_t* kr = kl + (uint64_t)slot * row_stride;
+    for (int i = 0; i < KLds<kFp8>::kLoads; ++i) {
+      const int row = kRowsPerLoad * i + lane / kLanesPerRow;
+      const int piece = (lane % kLanesPerRow) ^ KLds<kFp8>::swz(row);
+      const uint32_t slot = (uint32_t)(base + row < npos ? h.k[i] + (row & 3) : slot0);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(kbase + (uint64_t)slot * row_stride + 16 * piece),
+          (__attribute__((address_space(3))) void*)(klds + 1024 * i), 16, 0, kNt ? 2 : 0);
+    }
+  } else {
+    const uint8_t* kl = kbase + 16 * kg;      // this lane's bytes inside a K row: 64w + 16kg
 #pragma unroll
-    for (int w = 0; w < (kFp8 ? 2 : 4); ++w) ch.k[t][w] = kv_load<kNt, u32x4>(kr + 64 * w);
+    for (int t = 0; t < 2; ++t) {
+      const int i = base + 16 * t + j;
+      const uint32_t slot = (uint32_t)(i < npos ? h.k[t] + (j & 3) : slot0);
+      const uint8_t* kr = kl + (uint64_t)slot * row_stride;
+#pragma unroll
+      for (int w = 0; w < (kFp8 ? 2 : 4); ++w) ch.k[t][w] = kv_load<kNt, u32x4>(kr + 64 * w);
+    }
   }
+  const uint8_t* vl = vbase + j * 8 * EB;     // this lane's bytes inside a V row
   uint32_t vm = 0;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -165,17 +233,34 @@ __device__ __forceinline__ void issue_chunk(ChunkRaw<kFp8>& ch, const ChunkHeads
   ch.vmask = vm;
 }
 
-template <bool kFp8>
-__device__ __forceinline__ void compute_chunk(const ChunkRaw<kFp8>& ch, const bf16x8 (&qb)[4], float sl2,
-                                              float& m_run, float& l_run, f32x4 (&o)[8]) {
-  // K operand (A): step kk takes the 8 dimensions kdim(kk, kg) of the lane's row.
+template <bool kFp8, bool kKL>
+__device__ __forceinline__ void compute_chunk(const ChunkRaw<kFp8, kKL>& ch, const uint8_t* klds,
+                                              const bf16x8 (&qb)[4], float sl2, float& m_run, float& l_run,
+                                              f32x4 (&o)[8], int j, int kg) {
+  // K operand (A): step kk takes the 8 dimensions kdim(kk, kg) of row 16t + j,
+  // the 16-byte piece 64w + 16kg of the row (w = kk for BF16, kk / 2 for FP8).
+  u32x4 kraw[2][kFp8 ? 2 : 4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (kKL) {
+      const int row = 16 * t + j;
+      const uint8_t* kr = klds + KLds<kFp8>::kRowBytes * row;
+#pragma unroll
+      for (int w = 0; w < (kFp8 ? 2 : 4); w += 2)
+        lds_read_2x_b128(kraw[t][w], kraw[t][w + 1], kr + 16 * ((4 * w + kg) ^ KLds<kFp8>::swz(row)),
+                         kr + 16 * ((4 * w + 4 + kg) ^ KLds<kFp8>::swz(row)));
+    } else {
+#pragma unroll
+      for (int w = 0; w < (kFp8 ? 2 : 4); ++w) kraw[t][w] = ch.k[kKL ? 0 : t][w];
+    }
+  }
   bf16x8 ka[2][4];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     if (kFp8) {
-      const uint32_t ws[8] = {ch.k[t][0].x, ch.k[t][0].y, ch.k[t][0].z, ch.k[t][0].w,
-                              ch.k[t][kFp8 ? 1 : 0].x, ch.k[t][kFp8 ? 1 : 0].y, ch.k[t][kFp8 ? 1 : 0].z,
-                              ch.k[t][kFp8 ? 1 : 0].w};
+      const uint32_t ws[8] = {kraw[t][0].x, kraw[t][0].y, kraw[t][0].z, kraw[t][0].w,
+                              kraw[t][kFp8 ? 1 : 0].x, kraw[t][kFp8 ? 1 : 0].y, kraw[t][kFp8 ? 1 : 0].z,
+                              kraw[t][kFp8 ? 1 : 0].w};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const u32x2 lo = fp8x4_to_bf16x4(ws[2 * kk]), hi = fp8x4_to_bf16x4(ws[2 * kk + 1]);
@@ -183,7 +268,7 @@ __device__ __forceinline__ void compute_chunk(const ChunkRaw<kFp8>& ch, const bf
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) ka[t][kk] = __builtin_bit_cast(bf16x8, ch.k[t][kk & (kFp8 ? 1 : 3)]);
+      for (int kk = 0; kk < 4; ++kk) ka[t][kk] = __builtin_bit_cast(bf16x8, kraw[t][kk & (kFp8 ? 1 : 3)]);
     }
   }
   // V rows as 8 bf16 each.
@@ -256,14 +341,24 @@ __device__ __forceinline__ void compute_chunk(const ChunkRaw<kFp8>& ch, const bf
   }
 }
 
+// s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory
+// operations are outstanding / until all LDS operations are done.
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+constexpr int kWaitLds = 0xC07F;
+
 template <bool kFp8, bool kOutBf16, bool kNt>
 __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   constexpr int D = QSA_HEAD_DIM;
   constexpr int EB = kFp8 ? 1 : 2;            // bytes per KV element
+  using KL = KLds<kFp8>;
+  // The waves' K chunk buffers (two separate arrays, so that the compiler can
+  // tell the direct-to-LDS loads into one from the reads of the other).
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf_a[kAttnWaves][KL::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf_b[kAttnWaves][kFp8 ? KL::kBytes : 16];
   __shared__ float o_s[kAttnWaves][16][kOStride];
   __shared__ float m_s[kAttnWaves][16], l_s[kAttnWaves][16];
   __shared__ float ml_s[kMaxSplits][32];
-  __shared__ int heads_s[kMaxHeads];
+  __shared__ __attribute__((aligned(16))) int heads_s[kMaxHeads];
   __shared__ int s_last;
 
   // 1-D grid, query fastest, then KV head, then split: the last split of
@@ -317,40 +412,60 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
 #pragma unroll
   for (int u = 0; u < 8; ++u) o[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Main loop.  FP8: two register buffers in ping-pong, the next chunk's K/V
-  // loads are in flight while this chunk is computed.  BF16 (twice the bytes per
+  // Main loop.  With kKL (the non-temporal, large-batch kernels) a chunk's K
+  // rows go to the wave's LDS buffer through direct-to-LDS loads of whole
+  // lines and its V rows to registers; otherwise both go to registers.
+  // FP8: two chunk buffers in ping-pong, the next chunk's loads are in flight
+  // while this chunk is computed (with kKL an issue is always KL::kLoads + 8
+  // vector-memory operations, so waiting for that many to remain outstanding
+  // means the current chunk has landed; the compiler does not track the LDS
+  // the loads write, so these waits are explicit).  BF16 (twice the bytes per
   // chunk) keeps one chunk per wave in flight and relies on more waves.
+  constexpr bool kKL = kNt;
+  uint8_t* kbuf0 = kbuf_a[wave];
   if (kFp8) {
     // sched_barrier keeps the compiler from sinking a chunk's loads down to
     // its compute (which would serialise load latency and math again).
-    ChunkRaw<kFp8> ca, cb;
+    uint8_t* kbuf1 = kbuf_b[wave];
+    constexpr int kIssueOps = KL::kLoads + 8;
+    ChunkRaw<kFp8, kKL> ca, cb;
     const int nl = cfirst < c_end ? npos : 0;
-    issue_chunk<kFp8, kNt>(ca, lds_heads(heads_s, cfirst - c0, p.cps, j, kg), cfirst * kChunk, nl, slot0, kbase, vbase,
-                      row_stride, j, kg);
+    issue_chunk<kFp8, kNt, kKL>(ca, kbuf0, lds_heads<kFp8, kKL>(heads_s, cfirst - c0, p.cps, lane, j, kg),
+                                cfirst * kChunk, nl, slot0, kbase, vbase, row_stride, lane, j, kg);
     __builtin_amdgcn_sched_barrier(0);
     for (int c = cfirst; c < c_end; c += 2 * kAttnWaves) {
       const int cn = c + kAttnWaves;
-      issue_chunk<kFp8, kNt>(cb, lds_heads(heads_s, cn - c0, p.cps, j, kg), cn * kChunk, cn < c_end ? npos : 0, slot0,
-                        kbase, vbase, row_stride, j, kg);
+      issue_chunk<kFp8, kNt, kKL>(cb, kbuf1, lds_heads<kFp8, kKL>(heads_s, cn - c0, p.cps, lane, j, kg),
+                                  cn * kChunk, cn < c_end ? npos : 0, slot0, kbase, vbase, row_stride, lane, j, kg);
       __builtin_amdgcn_sched_barrier(0);
-      compute_chunk<kFp8>(ca, qb, sl2, m_run, l_run, o);
+      if (kKL) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kIssueOps));
+      compute_chunk<kFp8, kKL>(ca, kbuf0, qb, sl2, m_run, l_run, o, j, kg);
+      if (kKL) __builtin_amdgcn_s_waitcnt(kWaitLds);       // buffer 0 read out before it is refilled
       __builtin_amdgcn_sched_barrier(0);
       if (cn >= c_end) break;
       const int cnn = cn + kAttnWaves;
-      issue_chunk<kFp8, kNt>(ca, lds_heads(heads_s, cnn - c0, p.cps, j, kg), cnn * kChunk, cnn < c_end ? npos : 0,
-                        slot0, kbase, vbase, row_stride, j, kg);
+      issue_chunk<kFp8, kNt, kKL>(ca, kbuf0, lds_heads<kFp8, kKL>(heads_s, cnn - c0, p.cps, lane, j, kg),
+                                  cnn * kChunk, cnn < c_end ? npos : 0, slot0, kbase, vbase, row_stride, lane, j,
+                                  kg);
       __builtin_amdgcn_sched_barrier(0);
-      compute_chunk<kFp8>(cb, qb, sl2, m_run, l_run, o);
+      if (kKL) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kIssueOps));
+      compute_chunk<kFp8, kKL>(cb, kbuf1, qb, sl2, m_run, l_run, o, j, kg);
+      if (kKL) __builtin_amdgcn_s_waitcnt(kWaitLds);       // buffer 1 read out before it is refilled
       __builtin_amdgcn_sched_barrier(0);
     }
   } else {
     for (int c = cfirst; c < c_end; c += kAttnWaves) {
-      ChunkRaw<kFp8> cur;
-      issue_chunk<kFp8, kNt>(cur, lds_heads(heads_s, c - c0, p.cps, j, kg), c * kChunk, npos, slot0, kbase, vbase,
-                        row_stride, j, kg);
-      compute_chunk<kFp8>(cur, qb, sl2, m_run, l_run, o);
+      ChunkRaw<kFp8, kKL> cur;
+      issue_chunk<kFp8, kNt, kKL>(cur, kbuf0, lds_heads<kFp8, kKL>(heads_s, c - c0, p.cps, lane, j, kg), c * kChunk,
+                                  npos, slot0, kbase, vbase, row_stride, lane, j, kg);
+      if (kKL) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      compute_chunk<kFp8, kKL>(cur, kbuf0, qb, sl2, m_run, l_run, o, j, kg);
+      if (kKL) __builtin_amdgcn_s_waitcnt(kWaitLds);
     }
   }
+  // The last prefetch of a FP8 wave (a masked chunk past the end) may still
+  // be writing LDS: drain it before the workgroup can finish.
+  if (kKL) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
 
   // Row sums over the 4 lane groups of a head.
   l_run += __shfl_xor(l_run, 16, kWave);
