@@ -346,8 +346,10 @@ __device__ __forceinline__ void compute_chunk(const ChunkRaw<kFp8, kKL>& ch, con
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 constexpr int kWaitLds = 0xC07F;
 
+constexpr int kAttnThreads = 64 * kAttnWaves;
+
 template <bool kFp8, bool kOutBf16, bool kNt>
-__global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   constexpr int D = QSA_HEAD_DIM;
   constexpr int EB = kFp8 ? 1 : 2;            // bytes per KV element
   using KL = KLds<kFp8>;
@@ -361,16 +363,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) int heads_s[kMaxHeads];
   __shared__ int s_last;
 
-  // 1-D grid, query fastest, then KV head, then split: the last split of
-  // every unit, which holds only the few positions past the last full
-  // 4-chunk group, is dispatched last, so when the grid has more workgroups
-  // than the chip has CUs it is those nearly empty workgroups that share a
-  // CU with another.
+  // Grid (query, KV head, split), dispatched query fastest and split
+  // slowest: the last split of every unit, which holds only the few
+  // positions past the last full 4-chunk group, is dispatched last, so when
+  // the grid has more workgroups than the chip has CUs it is those nearly
+  // empty workgroups that share a CU with another.
   const int Hkv = p.num_kv_heads;
-  const int num_q = (int)(gridDim.x / (unsigned)(Hkv * p.splits));
-  const int q = blockIdx.x % num_q;
-  const int g = (blockIdx.x / num_q) % Hkv;
-  const int s = blockIdx.x / (num_q * Hkv);
+  const int q = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int j = lane & 15, kg = lane >> 4;
   const int G = p.group;
@@ -380,9 +379,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   const int c0 = s * p.cps;                 // first chunk of this workgroup's split
   const int cfirst = c0 + wave;
 
-  // Prologue: the block heads of the split go to LDS (one coalesced round),
-  // together with the query, the valid length and the first slot.
-  for (int h = tid; h < 8 * p.cps; h += blockDim.x) {
+  // Prologue: the block heads of the split go to LDS, the query rows to
+  // registers, with the valid length and the first slot; every load is
+  // issued before any is waited for (one memory round trip).
+  for (int h = tid; h < 8 * p.cps; h += kAttnThreads) {
     const int i = 4 * (8 * c0 + h);
     heads_s[h] = i < p.width ? prow[i] : 0;
   }
@@ -488,7 +488,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
 
   const int nout = G * D;
   if (p.splits == 1) {
-    for (int idx = tid; idx < nout; idx += blockDim.x) {
+    for (int idx = tid; idx < nout; idx += kAttnThreads) {
       const int hh = idx / D, d = idx % D;
       float M = -INFINITY;
 #pragma unroll
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
   float* unit = p.part + ((int64_t)q * Hkv + g) * p.splits * pstride;
   const __amdgpu_buffer_rsrc_t unit_rs = partial_rsrc(unit);
   const int mine = s * pstride;
-  for (int v4 = tid; v4 < (nout + 32) / 4; v4 += blockDim.x) {
+  for (int v4 = tid; v4 < (nout + 32) / 4; v4 += kAttnThreads) {
     f32x4 val;
     if (4 * v4 < nout) {
       const int hh = (4 * v4) / D, d = (4 * v4) % D;
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnParams p) {
     const int t = tid / 8, r4 = tid % 8;
     *reinterpret_cast<f32x4*>(&ml_s[t][4 * r4]) = load_coherent(unit_rs, t * pstride + nout + 4 * r4);
   }
-  for (int v0 = 0; v0 < nout / 4; v0 += blockDim.x) {
+  for (int v0 = 0; v0 < nout / 4; v0 += kAttnThreads) {
     const int v4 = v0 + tid;
     f32x4 vals[kMaxSplits];
 #pragma unroll
@@ -635,15 +635,15 @@ hipError_t launch_attn(const Meta& m, const AttnArgs& a, hipStream_t stream) {
   p.sm_scale_log2 = a.sm_scale * 1.4426950408889634f;
   p.splits = sp.splits;
   p.cps = sp.chunks_per_split;
-  const dim3 grid((unsigned)((int64_t)m.num_q * sp.splits * a.num_kv_heads));
+  const dim3 grid((unsigned)m.num_q, (unsigned)a.num_kv_heads, (unsigned)sp.splits);
   // Large batches stream K/V with non-temporal loads (measured faster once
   // the (query, KV head) units alone fill the chip); small ones keep the
   // default policy (faster there).
   const bool nt = (int64_t)m.num_q * a.num_kv_heads >= kNtMinUnits;
 #define QSA_ATTN_LAUNCH(F8, OB)                                              \
   do {                                                                        \
-    if (nt) attn_kernel<F8, OB, true><<<grid, 256, 0, stream>>>(p);           \
-    else attn_kernel<F8, OB, false><<<grid, 256, 0, stream>>>(p);             \
+    if (nt) attn_kernel<F8, OB, true><<<grid, kAttnThreads, 0, stream>>>(p);           \
+    else attn_kernel<F8, OB, false><<<grid, kAttnThreads, 0, stream>>>(p);             \
   } while (0)
   if (a.kv_fp8) {
     if (a.out_bf16) QSA_ATTN_LAUNCH(true, true);

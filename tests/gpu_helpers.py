@@ -37,24 +37,38 @@ def oracle_decode(w, **kw):
                          w.k_cache, w.v_cache, w.kv_dtype, w.k_scale, w.v_scale, sm_scale=SM_SCALE, **kw)
 
 
-def run_decode(w, dev=None, out_dtype=torch.float32, k=qsa.TOPK, ws=None):
+def run_decode(w, dev=None, out_dtype=torch.float32, k=qsa.TOPK, ws=None, debug=True):
+    """Fused qsa_decode.  debug=True also asks for sel / n_sel / pos; without
+    them (the production call) only out and n_pos come back."""
     dev = upload(w) if dev is None else dev
     b = batch_of(w)
     hq = w.num_q_heads
     width = 4 * k + 3
     out = torch.full((w.num_q, hq, 128), float("nan"), dtype=out_dtype, device="cuda")
-    sel = torch.full((w.num_q, k), -7, dtype=torch.int32, device="cuda")
-    n_sel = torch.full((w.num_q,), -7, dtype=torch.int32, device="cuda")
-    pos = torch.full((w.num_q, width), -7, dtype=torch.int32, device="cuda")
     n_pos = torch.full((w.num_q,), -7, dtype=torch.int32, device="cuda")
     ws = qsa.alloc_workspace(b, hq, w.num_kv_heads, k) if ws is None else ws
+    extra = {}
+    if debug:
+        extra = {"sel": torch.full((w.num_q, k), -7, dtype=torch.int32, device="cuda"),
+                 "n_sel": torch.full((w.num_q,), -7, dtype=torch.int32, device="cuda"),
+                 "pos": torch.full((w.num_q, width), -7, dtype=torch.int32, device="cuda")}
     qsa.qsa_decode(b, dev["idx_q"], dev["ckeys"], dev["q"], dev["k_cache"], dev["v_cache"], out, ws,
-                   k_scale=dev["k_scale"], v_scale=dev["v_scale"], k=k, sm_scale=SM_SCALE,
-                   sel=sel, n_sel=n_sel, pos=pos, n_pos=n_pos)
+                   k_scale=dev["k_scale"], v_scale=dev["v_scale"], k=k, sm_scale=SM_SCALE, n_pos=n_pos, **extra)
     torch.cuda.synchronize()
-    return {"out": out.float().cpu().numpy().astype(np.float64), "sel": sel.cpu().numpy(),
-            "n_sel": n_sel.cpu().numpy(), "pos": pos.cpu().numpy(), "n_pos": n_pos.cpu().numpy(),
-            "ws": ws}
+    res = {"out": out.float().cpu().numpy().astype(np.float64), "n_pos": n_pos.cpu().numpy(), "ws": ws}
+    for key, t in extra.items():
+        res[key] = t.cpu().numpy()
+    return res
+
+
+def assert_lean_decode_same(w, got, dev=None, k=qsa.TOPK, out_dtype=torch.float32):
+    """The production call (no sel / n_sel / pos requested, as a serving loop
+    makes it) gives the same n_pos and the same output bits as the checked
+    call."""
+    lean = run_decode(w, dev, out_dtype=out_dtype, k=k, debug=False)
+    assert np.array_equal(lean["n_pos"], got["n_pos"])
+    assert np.array_equal(lean["out"].view(np.uint64), got["out"].view(np.uint64))
+    return lean
 
 
 def assert_selection_equal(got, ref, queries=None):

@@ -10,7 +10,8 @@ import torch
 import oracle
 from workloads import make_workload
 from workloads.device import upload
-from gpu_helpers import assert_out_close, assert_selection_equal, need_gpu, oracle_decode, run_decode, say
+from gpu_helpers import (assert_lean_decode_same, assert_out_close, assert_selection_equal, need_gpu, oracle_decode,
+                         run_decode, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +30,7 @@ def test_config_parity(name):
     got = run_decode(w, dev)
     assert_selection_equal(got, ref)
     assert_out_close(got["out"], ref["out"])
+    assert_lean_decode_same(w, got, dev)
     if name.startswith("mtp262k_ties"):
         # closed form: the 512 lowest-index blocks of the tie set that are full for the query
         tie = w.meta["tie_sets"][0]

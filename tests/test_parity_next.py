@@ -93,6 +93,11 @@ def _decode_paged(w, page_size, seed, dev=None):
     ws = qsa.alloc_workspace(b, hq, w.num_kv_heads, k)
     qsa.qsa_decode(b, d["idx_q"], d["ckeys"], d["q"], d["k_cache"], d["v_cache"], out, ws, k_scale=d["k_scale"],
                    v_scale=d["v_scale"], sm_scale=SM_SCALE, sel=sel, n_sel=n_sel, pos=pos, n_pos=n_pos)
+    # the production call (no sel / n_sel / pos requested)
+    out_lean = torch.full_like(out, float("nan"))
+    n_pos_lean = torch.full_like(n_pos, -7)
+    qsa.qsa_decode(b, d["idx_q"], d["ckeys"], d["q"], d["k_cache"], d["v_cache"], out_lean, ws,
+                   k_scale=d["k_scale"], v_scale=d["v_scale"], sm_scale=SM_SCALE, n_pos=n_pos_lean)
     # the stage path: selection without positions, then the index builder
     pos2 = torch.full_like(pos, -7)
     n_pos2 = torch.full_like(n_pos, -7)
@@ -101,6 +106,8 @@ def _decode_paged(w, page_size, seed, dev=None):
     res = {"out": out.cpu().numpy().astype(np.float64), "sel": sel.cpu().numpy(), "n_sel": n_sel.cpu().numpy(),
            "pos": pos.cpu().numpy(), "n_pos": n_pos.cpu().numpy()}
     assert np.array_equal(pos2.cpu().numpy(), res["pos"]) and np.array_equal(n_pos2.cpu().numpy(), res["n_pos"])
+    assert np.array_equal(n_pos_lean.cpu().numpy(), res["n_pos"])
+    assert np.array_equal(out_lean.cpu().numpy().view(np.uint32), out.cpu().numpy().view(np.uint32))
     return res, table, kc, vc
 
 

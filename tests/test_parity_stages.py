@@ -10,7 +10,7 @@ import block_sparse_attention_qsa_amd as qsa
 import oracle
 from workloads import make_custom
 from workloads.device import upload
-from gpu_helpers import (SM_SCALE, assert_out_close, assert_selection_equal, batch_of, need_gpu, oracle_decode,
+from gpu_helpers import (SM_SCALE, assert_lean_decode_same, assert_out_close, assert_selection_equal, batch_of, need_gpu, oracle_decode,
                          run_decode, say)
 
 pytestmark = pytest.mark.gpu
@@ -209,6 +209,7 @@ def test_decode_small_mixed():
         got = run_decode(w)
         assert_selection_equal(got, ref)
         assert_out_close(got["out"], ref["out"])
+        assert_lean_decode_same(w, got)
         # split-arrival counters sit at the start of the workspace and are reset by the call
         assert int(got["ws"][:w.num_q * w.num_kv_heads * 128].sum()) == 0
 
@@ -228,6 +229,7 @@ def test_decode_edge_lengths_dense_equivalence():
     got = run_decode(w)
     assert_selection_equal(got, ref)
     assert_out_close(got["out"], ref["out"])
+    assert_lean_decode_same(w, got)
     # length 1: the output is the single V row itself
     for r in range(w.num_req):
         if int(w.seq_len[r]) == 1:
@@ -245,6 +247,7 @@ def test_decode_small_k():
         got = run_decode(w, k=k)
         assert_selection_equal(got, ref)
         assert_out_close(got["out"], ref["out"])
+        assert_lean_decode_same(w, got, k=k)
 
 
 def test_decode_deterministic_and_workspace_reusable():
@@ -259,3 +262,10 @@ def test_decode_deterministic_and_workspace_reusable():
     for x in (b, c):
         assert np.array_equal(a["out"].view(np.uint64), x["out"].view(np.uint64))
         assert np.array_equal(a["pos"], x["pos"])
+    # the production call on the same workspace, twice, then the checked call again
+    for _ in range(2):
+        lean = run_decode(w, dev, ws=a["ws"], debug=False)
+        assert np.array_equal(a["out"].view(np.uint64), lean["out"].view(np.uint64))
+    d = run_decode(w, dev, ws=a["ws"])
+    assert np.array_equal(a["out"].view(np.uint64), d["out"].view(np.uint64))
+    assert np.array_equal(a["pos"], d["pos"])
