@@ -46,6 +46,12 @@ __device__ __forceinline__ f32x4 load_coherent(__amdgpu_buffer_rsrc_t r, int flo
 __device__ __forceinline__ void store_coherent(__amdgpu_buffer_rsrc_t r, int float_off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, float_off * 4, 0, kCpolDevice);
 }
+__device__ __forceinline__ float load_coherent_f32(__amdgpu_buffer_rsrc_t r, int float_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, float_off * 4, 0, kCpolDevice));
+}
+__device__ __forceinline__ void store_coherent_f32(__amdgpu_buffer_rsrc_t r, int float_off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, float_off * 4, 0, kCpolDevice);
+}
 constexpr int kMaxHeads = 8 * ((QSA_WIDTH + kChunk - 1) / kChunk);   // block heads of one split
 constexpr float kRescaleSlack = 8.f;     // log2 headroom of the softmax reference maximum
 constexpr int kNtMinUnits = 256;         // (query, KV head) units from which K/V loads are non-temporal
@@ -359,7 +365,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf_b[kAttnWaves][kFp8 ? KL::kBytes : 16];
   __shared__ float o_s[kAttnWaves][16][kOStride];
   __shared__ float m_s[kAttnWaves][16], l_s[kAttnWaves][16];
-  __shared__ float ml_s[kMaxSplits][32];
   __shared__ __attribute__((aligned(16))) int heads_s[kMaxHeads];
   __shared__ int s_last;
 
@@ -516,38 +521,31 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   float* unit = p.part + ((int64_t)q * Hkv + g) * p.splits * pstride;
   const __amdgpu_buffer_rsrc_t unit_rs = partial_rsrc(unit);
   const int mine = s * pstride;
-  for (int v4 = tid; v4 < (nout + 32) / 4; v4 += kAttnThreads) {
-    f32x4 val;
-    if (4 * v4 < nout) {
-      const int hh = (4 * v4) / D, d = (4 * v4) % D;
-      float M = -INFINITY;
+  for (int v4 = tid; v4 < nout / 4; v4 += kAttnThreads) {
+    const int hh = (4 * v4) / D, d = (4 * v4) % D;
+    float M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, m_s[w][hh]);
-      val = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, m_s[w][hh]);
+    f32x4 val = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) {
-        const float sc = m_s[w][hh] == -INFINITY ? 0.f : exp2f(m_s[w][hh] - M);
-        val += sc * *reinterpret_cast<const f32x4*>(&o_s[w][hh][d]);
-      }
-    } else {
-      // m (heads 0..15) then l (heads 0..15), 4 heads per vector
-      const int r4 = 4 * v4 - nout;
-      const bool is_l = r4 >= 16;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int hh = (r4 & 15) + c;
-        float M = -INFINITY, den = 0.f;
-        if (hh < G) {
-#pragma unroll
-          for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, m_s[w][hh]);
-#pragma unroll
-          for (int w = 0; w < kAttnWaves; ++w)
-            den += (m_s[w][hh] == -INFINITY ? 0.f : exp2f(m_s[w][hh] - M)) * l_s[w][hh];
-        }
-        val[c] = is_l ? den : M;
-      }
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float sc = m_s[w][hh] == -INFINITY ? 0.f : exp2f(m_s[w][hh] - M);
+      val += sc * *reinterpret_cast<const f32x4*>(&o_s[w][hh][d]);
     }
     store_coherent(unit_rs, mine + 4 * v4, val);
+  }
+  // m (heads 0..15) then l (heads 0..15): one value per thread
+  if (tid < 32) {
+    const int hh = tid & 15;
+    float M = -INFINITY, den = 0.f;
+    if (hh < G) {
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, m_s[w][hh]);
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w)
+        den += (m_s[w][hh] == -INFINITY ? 0.f : exp2f(m_s[w][hh] - M)) * l_s[w][hh];
+    }
+    store_coherent_f32(unit_rs, mine + nout + tid, tid < 16 ? M : den);
   }
   __builtin_amdgcn_s_waitcnt(0);     // this thread's stores have reached the coherence point
   __syncthreads();
@@ -558,38 +556,35 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   __syncthreads();
   if (!s_last) return;
 
-  // Last workgroup of the unit: 16-byte device-scope loads bring every
-  // split's maxima, sums and numerators (one round for groups of <= 8 heads).
-  // Each thread then weighs the splits of its own head from LDS itself (the
-  // 2*S reads are independent, so they overlap), with no further barrier.
+  // Last workgroup of the unit: device-scope loads bring, straight into
+  // each thread's registers, every split's numerators of the thread's 4
+  // outputs and the maxima and sums of its head (one round for groups of
+  // <= 8 heads; splits past S re-read the last one and are not weighed).
   const int S = p.splits;
-  if (tid < S * 8) {
-    const int t = tid / 8, r4 = tid % 8;
-    *reinterpret_cast<f32x4*>(&ml_s[t][4 * r4]) = load_coherent(unit_rs, t * pstride + nout + 4 * r4);
-  }
   for (int v0 = 0; v0 < nout / 4; v0 += kAttnThreads) {
-    const int v4 = v0 + tid;
+    const int v4 = min(v0 + tid, nout / 4 - 1);
+    const int hh = (4 * v4) / D;
     f32x4 vals[kMaxSplits];
+    float mt[kMaxSplits], lt[kMaxSplits];
 #pragma unroll
-    for (int t = 0; t < kMaxSplits; ++t)
-      vals[t] = (t < S && v4 < nout / 4) ? load_coherent(unit_rs, t * pstride + 4 * v4)
-                                         : f32x4{0.f, 0.f, 0.f, 0.f};
-    if (v0 == 0) __syncthreads();
-    if (v4 < nout / 4) {
-      const int hh = (4 * v4) / D;
-      float mt[kMaxSplits], M = -INFINITY;
+    for (int t = 0; t < kMaxSplits; ++t) {
+      const int off = min(t, S - 1) * pstride;
+      vals[t] = load_coherent(unit_rs, off + 4 * v4);
+      mt[t] = load_coherent_f32(unit_rs, off + nout + hh);
+      lt[t] = load_coherent_f32(unit_rs, off + nout + 16 + hh);
+    }
+    if (v0 + tid < nout / 4) {
+      float M = -INFINITY;
 #pragma unroll
-      for (int t = 0; t < kMaxSplits; ++t) {
-        mt[t] = t < S ? ml_s[t][hh] : -INFINITY;
-        M = fmaxf(M, mt[t]);
-      }
+      for (int t = 0; t < kMaxSplits; ++t)
+        if (t < S) M = fmaxf(M, mt[t]);
       f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
       float den = 0.f;
 #pragma unroll
       for (int t = 0; t < kMaxSplits; ++t) {
         if (t < S) {
           const float wgt = mt[t] == -INFINITY ? 0.f : exp2f(mt[t] - M);
-          den += wgt * ml_s[t][16 + hh];
+          den += wgt * lt[t];
           num += wgt * vals[t];
         }
       }
