@@ -14,6 +14,10 @@ using qsa::Meta;
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// Largest score row stride qsa_score takes: the four rows of a request are
+// addressed by 32-bit byte offsets from its first one.
+constexpr int64_t kMaxScoreLd = int64_t(1) << 26;
+
 struct WsLayout {
   size_t counters, partials, attn_end, scores, sel, n_sel, pos, n_pos, msel, total;
 };
@@ -129,7 +133,7 @@ qsa_status qsa_score(const qsa_batch* batch, const void* idx_q, const void* ckey
                      hipStream_t stream) {
   QSA_TRY(check_batch(batch));
   if (!idx_q || !ckeys || !scores) return QSA_ERR_NULL;
-  if (ld < batch->max_blocks) return QSA_ERR_SHAPE;
+  if (ld < batch->max_blocks || ld > kMaxScoreLd) return QSA_ERR_SHAPE;
   return launched(qsa::launch_score(meta_of(batch), idx_q, ckeys, scores, ld, stream));
 }
 

@@ -19,14 +19,25 @@ namespace qsa {
 constexpr int kScoreWaves = 4;             // waves per workgroup
 
 // Store the scores of rows row .. row+3 below nblk (one 16-byte store when
-// the score rows are 16-byte aligned).
-__device__ __forceinline__ void store_scores(float* qrow, f32x4 acc, bool vec, int row, int nblk) {
+// the score rows are 16-byte aligned) at byte qoff + 4 * row of the buffer
+// rs.  With kWt the stores are device-scope (they write through the L2),
+// so the end of the kernel does not have a few MB of dirty L2 lines to
+// write back before the selection can start: −0.5 µs per step for a
+// 32-request batch, +0.7 µs for one 1M-token request, whose four long rows
+// stream better through the L2.
+template <bool kWt>
+__device__ __forceinline__ void store_scores(__amdgpu_buffer_rsrc_t rs, uint32_t qoff, f32x4 acc, bool vec, int row,
+                                             int nblk) {
+  constexpr int kCpol = kWt ? kCpolDevice : 0;
   if (vec && row + 3 < nblk) {
-    *reinterpret_cast<f32x4*>(qrow + row) = acc;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), rs, qoff + 4 * row, 0, kCpol);
   } else {
+    // (__float_as_uint of the element: a bit cast of a vector-element
+    // subscript reads element 0 with this compiler)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (row + i < nblk) qrow[row + i] = acc[i];
+      if (row + i < nblk)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i]), rs, qoff + 4 * (row + i), 0, kCpol);
   }
 }
 
@@ -35,6 +46,7 @@ __device__ __forceinline__ void store_scores(float* qrow, f32x4 acc, bool vec, i
 // to its own 4 KiB of LDS (direct-to-LDS loads, whole lines, non-temporal),
 // is read back into MFMA operands, and the next tile's loads are issued
 // into the same LDS before the current tile is contracted.
+template <bool kWt>
 __global__ __launch_bounds__(256) void score_kernel(Meta m, const uint16_t* __restrict__ idx_q,
                                                     const uint16_t* __restrict__ ckeys,
                                                     float* __restrict__ scores, int64_t ld, int vec) {
@@ -63,7 +75,11 @@ __global__ __launch_bounds__(256) void score_kernel(Meta m, const uint16_t* __re
   const bool qvalid = n < nq;
   bf16x8 qb[4];
   load_index_queries(qb, idx_q, qs, nq, n, g);
-  float* qrow = scores + (int64_t)(qs + (qvalid ? n : 0)) * ld;
+  // the request's first score row as the (wave-uniform) buffer base, each
+  // lane's query row as an offset
+  const __amdgpu_buffer_rsrc_t srs =
+      __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)qs * ld, 0, 0x7fffffff, 0x00020000);
+  const uint32_t qoff = (uint32_t)((qvalid ? n : 0) * ld * 4);
 
   for (;;) {
     __builtin_amdgcn_s_waitcnt(0);            // this wave's tile (and the queries) have landed
@@ -76,7 +92,7 @@ __global__ __launch_bounds__(256) void score_kernel(Meta m, const uint16_t* __re
     }
     __builtin_amdgcn_sched_barrier(0);
     const f32x4 sc = contract_key_tile(t, qb);
-    if (qvalid) store_scores(qrow, sc, vec != 0, tile * 16 + 4 * g, nblk);
+    if (qvalid) store_scores<kWt>(srs, qoff, sc, vec != 0, tile * 16 + 4 * g, nblk);
     if (next >= ntiles) break;
     tile = next;
   }
@@ -93,8 +109,10 @@ hipError_t launch_score(const Meta& m, const void* idx_q, const void* ckeys, flo
   if (gx > cap) gx = cap;
   const dim3 grid((unsigned)gx, (unsigned)m.num_req);
   const int vec = (ld % 4 == 0) && (reinterpret_cast<uintptr_t>(scores) % 16 == 0);
-  score_kernel<<<grid, 256, 0, stream>>>(m, static_cast<const uint16_t*>(idx_q),
-                                            static_cast<const uint16_t*>(ckeys), scores, ld, vec);
+  const uint16_t* iq = static_cast<const uint16_t*>(idx_q);
+  const uint16_t* ck = static_cast<const uint16_t*>(ckeys);
+  if (m.num_req > 1) score_kernel<true><<<grid, 256, 0, stream>>>(m, iq, ck, scores, ld, vec);
+  else score_kernel<false><<<grid, 256, 0, stream>>>(m, iq, ck, scores, ld, vec);
   return hipGetLastError();
 }
 

@@ -108,7 +108,7 @@ size_t qsa_workspace_bytes(const qsa_batch* batch, int32_t num_q_heads, int32_t 
 /* a1 - block scores.  For every query q of request r and every full block
  * b < seq_len[r] / 4:   scores[q * ld + b] = fp32( sum_d idx_q[q][d] * ckeys[blk_start[r] + b][d] ).
  * idx_q  [dev] BF16 [num_q][128] row-major; ckeys [dev] BF16 [rows][128] row-major;
- * scores [dev] FP32 [num_q][ld], ld >= max_blocks.  Products are exact and the sum is
+ * scores [dev] FP32 [num_q][ld], max_blocks <= ld <= 2^26.  Products are exact and the sum is
  * accumulated in FP32 (exact whenever all partial sums are integers below 2^24).
  * Each key row is read from memory once per request and used for all of its
  * queries.  Entries b >= seq_len[r] / 4 are not written. */

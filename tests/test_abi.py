@@ -63,6 +63,7 @@ def test_error_paths_return_before_launch():
     assert lib.qsa_score(None, P, P, P, 12500, None) == 1
     assert lib.qsa_score(ctypes.byref(good), None, P, P, 12500, None) == 1
     assert lib.qsa_score(ctypes.byref(good), P, P, P, 100, None) == 2          # ld < max_blocks
+    assert lib.qsa_score(ctypes.byref(good), P, P, P, (1 << 26) + 1, None) == 2  # ld past 2^26
     bad_q = _cbatch(num_req=1, num_q=5)
     assert lib.qsa_score(ctypes.byref(bad_q), P, P, P, 12500, None) == 2       # > 4 queries per request
     nullmeta = qsa._CBatch(1, 1, 10, 0, 0, 0, 0, 0, 0, 0)
