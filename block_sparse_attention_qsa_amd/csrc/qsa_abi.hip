@@ -78,6 +78,7 @@ qsa_status check_attn_args(const void* q, const void* kc, const void* vc, int32_
   if (kv_dtype != QSA_KV_BF16 && kv_dtype != QSA_KV_FP8_E4M3) return QSA_ERR_UNSUPPORTED;
   if (kv_dtype == QSA_KV_FP8_E4M3 && (!ks || !vs)) return QSA_ERR_NULL;
   if (out_dtype != QSA_OUT_F32 && out_dtype != QSA_OUT_BF16) return QSA_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(out) % (out_dtype == QSA_OUT_F32 ? 16 : 8) != 0) return QSA_ERR_SHAPE;
   if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return QSA_ERR_SHAPE;
   return QSA_OK;
 }

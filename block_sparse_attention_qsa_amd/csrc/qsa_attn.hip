@@ -347,6 +347,19 @@ __device__ __forceinline__ void compute_chunk(const ChunkRaw<kFp8, kKL>& ch, con
   }
 }
 
+// Four consecutive outputs (element oi onwards, oi a multiple of 4) as FP32
+// or BF16 (nearest-even conversion).
+template <bool kOutBf16>
+__device__ __forceinline__ void store_out(void* out, int64_t oi, f32x4 v) {
+  if (kOutBf16) {
+    const bf16x2 a = bf16x2{(__bf16)v.x, (__bf16)v.y}, b = bf16x2{(__bf16)v.z, (__bf16)v.w};
+    *reinterpret_cast<u32x2*>(static_cast<__bf16*>(out) + oi) =
+        u32x2{__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b)};
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + oi) = v;
+  }
+}
+
 // s_waitcnt immediates (gfx9 encoding): wait until at most n vector-memory
 // operations are outstanding / until all LDS operations are done.
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x70 | 0xF00; }
@@ -493,22 +506,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
 
   const int nout = G * D;
   if (p.splits == 1) {
-    for (int idx = tid; idx < nout; idx += kAttnThreads) {
-      const int hh = idx / D, d = idx % D;
+    // 4 consecutive outputs of one head per thread
+    for (int v4 = tid; v4 < nout / 4; v4 += kAttnThreads) {
+      const int hh = (4 * v4) / D, d = (4 * v4) % D;
       float M = -INFINITY;
 #pragma unroll
       for (int w = 0; w < kAttnWaves; ++w) M = fmaxf(M, m_s[w][hh]);
-      float num = 0.f, den = 0.f;
+      f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+      float den = 0.f;
 #pragma unroll
       for (int w = 0; w < kAttnWaves; ++w) {
         const float sc = m_s[w][hh] == -INFINITY ? 0.f : exp2f(m_s[w][hh] - M);
-        num += sc * o_s[w][hh][d];
+        num += sc * *reinterpret_cast<const f32x4*>(&o_s[w][hh][d]);
         den += sc * l_s[w][hh];
       }
-      const float val = num / den * vscale;
-      const int64_t oi = ((int64_t)q * Hq + g * G + hh) * D + d;
-      if (kOutBf16) static_cast<__bf16*>(p.out)[oi] = (__bf16)val;
-      else static_cast<float*>(p.out)[oi] = val;
+      num *= vscale / den;
+      store_out<kOutBf16>(p.out, ((int64_t)q * Hq + g * G) * D + 4 * v4, num);
     }
     return;
   }
@@ -589,16 +602,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
         }
       }
       num *= vscale / den;
-      const int64_t oi = ((int64_t)q * Hq + g * G) * D + 4 * v4;
-      if (kOutBf16) {
-        __bf16* op = static_cast<__bf16*>(p.out) + oi;
-        op[0] = (__bf16)num.x;
-        op[1] = (__bf16)num.y;
-        op[2] = (__bf16)num.z;
-        op[3] = (__bf16)num.w;
-      } else {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(p.out) + oi) = num;
-      }
+      store_out<kOutBf16>(p.out, ((int64_t)q * Hq + g * G) * D + 4 * v4, num);
     }
   }
   if (tid == 0) p.counters[(q * Hkv + g) * kCounterStride] = 0u;

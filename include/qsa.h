@@ -149,7 +149,8 @@ qsa_status qsa_build_index(const qsa_batch* batch, const int32_t* sel, const int
  * k_scale[g] (likewise V with v_scale).  q [dev] BF16 [num_q][Hq][128];
  * k_cache, v_cache [dev] [slots][Hkv][128] of BF16 or FP8; k_scale, v_scale [dev]
  * FP32 [Hkv], required for FP8 and ignored for BF16; pos, n_pos as from
- * qsa_build_index with width = 4k+3; out [dev] [num_q][Hq][128] FP32 or BF16.
+ * qsa_build_index with width = 4k+3; out [dev] [num_q][Hq][128] FP32 (16-byte aligned) or
+ * BF16 (8-byte aligned); a misaligned out is QSA_ERR_SHAPE.
  * Hq % Hkv == 0 and Hq / Hkv <= 16.  ws: qsa_workspace_bytes() for this k. */
 qsa_status qsa_sparse_attn(const qsa_batch* batch, const void* q, const void* k_cache,
                            const void* v_cache, int32_t kv_dtype, const float* k_scale,

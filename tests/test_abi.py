@@ -91,6 +91,11 @@ def test_error_paths_return_before_launch():
     assert args(32, 4, 0, None, 2051, 0.08, 2, P, 1 << 30) == 3
     assert args(32, 4, 0, None, 2051, 0.08, 0, None, 0) == 4                 # workspace needed
     assert args(32, 4, 0, None, 2051, 0.08, 0, ctypes.c_void_p(0x1004), 1 << 30) == 4   # misaligned
+    # output alignment: 16 bytes for FP32, 8 for BF16
+    att_out = lambda out, odt: lib.qsa_sparse_attn(ctypes.byref(good), P, P, P, 0, None, None, 32, 4, P, P, 2051,
+                                                   0.08, out, odt, P, 1 << 30, None)
+    assert att_out(ctypes.c_void_p(0x1008), 0) == 2
+    assert att_out(ctypes.c_void_p(0x1004), 1) == 2
     d = lambda ws, wsn: lib.qsa_decode(ctypes.byref(good), P, P, P, P, P, 0, None, None, 32, 4, 512, 0.08, P, 0,
                                        None, None, None, None, ws, wsn, None)
     assert d(P, 16) == 4
