@@ -347,6 +347,28 @@ __device__ __forceinline__ void compute_chunk(const ChunkRaw<kFp8, kKL>& ch, con
   }
 }
 
+// Maximum / sum over the 32 lanes of the wave half this lane is in (every
+// lane of the half gets it).
+__device__ __forceinline__ float half32_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  const float lo = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16)));
+  const float hi = fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
+                         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48)));
+  return lane_id() >= 32 ? hi : lo;
+}
+__device__ __forceinline__ float half32_sum(float v) {
+  v = row16_sum(v);
+  const float lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)) +
+                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return lane_id() >= 32 ? hi : lo;
+}
+
 // Four consecutive outputs (element oi onwards, oi a multiple of 4) as FP32
 // or BF16 (nearest-even conversion).
 template <bool kOutBf16>
@@ -570,37 +592,39 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   if (!s_last) return;
 
   // Last workgroup of the unit: device-scope loads bring, straight into
-  // each thread's registers, every split's numerators of the thread's 4
-  // outputs and the maxima and sums of its head (one round for groups of
-  // <= 8 heads; splits past S re-read the last one and are not weighed).
+  // registers, every split's numerators of each thread's 4 outputs (one
+  // round for groups of <= 8 heads; splits past S re-read the last one and
+  // are not weighed).  The 32 lanes of a wave half share one head (128
+  // outputs): lane t of the half loads split t's maximum and sum of that
+  // head, the half reduces them, and each lane reads the split weights from
+  // the lanes that hold them.
   const int S = p.splits;
+  const bool upper = lane >= 32;
+  const int tl = lane & 31;
+  static_assert(kMaxSplits <= 32, "one split per lane of a wave half");
   for (int v0 = 0; v0 < nout / 4; v0 += kAttnThreads) {
     const int v4 = min(v0 + tid, nout / 4 - 1);
     const int hh = (4 * v4) / D;
     f32x4 vals[kMaxSplits];
-    float mt[kMaxSplits], lt[kMaxSplits];
+#pragma unroll
+    for (int t = 0; t < kMaxSplits; ++t) vals[t] = load_coherent(unit_rs, min(t, S - 1) * pstride + 4 * v4);
+    const int ts = min(tl, S - 1) * pstride + nout + hh;
+    const float m_own = load_coherent_f32(unit_rs, ts);
+    const float l_own = load_coherent_f32(unit_rs, ts + 16);
+    const float mv = tl < S ? m_own : -INFINITY;
+    const float M = half32_max(mv);
+    const float w_own = mv == -INFINITY ? 0.f : exp2f(mv - M);
+    const float den = half32_sum(tl < S ? w_own * l_own : 0.f);
+    f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < kMaxSplits; ++t) {
-      const int off = min(t, S - 1) * pstride;
-      vals[t] = load_coherent(unit_rs, off + 4 * v4);
-      mt[t] = load_coherent_f32(unit_rs, off + nout + hh);
-      lt[t] = load_coherent_f32(unit_rs, off + nout + 16 + hh);
+      if (t < S) {
+        const float w_lo = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_own), t));
+        const float w_hi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w_own), 32 + t));
+        num += (upper ? w_hi : w_lo) * vals[t];
+      }
     }
     if (v0 + tid < nout / 4) {
-      float M = -INFINITY;
-#pragma unroll
-      for (int t = 0; t < kMaxSplits; ++t)
-        if (t < S) M = fmaxf(M, mt[t]);
-      f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
-      float den = 0.f;
-#pragma unroll
-      for (int t = 0; t < kMaxSplits; ++t) {
-        if (t < S) {
-          const float wgt = mt[t] == -INFINITY ? 0.f : exp2f(mt[t] - M);
-          den += wgt * lt[t];
-          num += wgt * vals[t];
-        }
-      }
       num *= vscale / den;
       store_out<kOutBf16>(p.out, ((int64_t)q * Hq + g * G) * D + 4 * v4, num);
     }
