@@ -83,6 +83,13 @@ def _select_case(nfs, kind, seed):
             s = rng.standard_normal(nf).astype(np.float32)
             s[rng.random(nf) < 0.01] = np.inf
             s[rng.random(nf) < 0.01] = -np.inf
+        elif kind == "spiky":
+            # a flat row with a few hundred high outliers: the value range is
+            # set by the outliers, so almost the whole row shares the lowest
+            # few grid bins and every outlier is kept
+            s = (rng.standard_normal(nf) * 0.01).astype(np.float32)
+            hot = rng.choice(nf, min(nf, 300), replace=False)
+            s[hot] = rng.integers(10, 21, len(hot)).astype(np.float32)
         elif kind == "flat":
             # 60% of the blocks share the top score: the chosen top-level radix
             # bin can exceed what the selector stages in LDS
@@ -105,7 +112,7 @@ SELECT_GROUPS = {
 
 
 @pytest.mark.parametrize("group", list(SELECT_GROUPS))
-@pytest.mark.parametrize("kind", ["ties", "normal", "zeros", "wide", "flat", "inf"])
+@pytest.mark.parametrize("kind", ["ties", "normal", "zeros", "wide", "flat", "inf", "spiky"])
 def test_select_bit_exact(kind, group):
     need_gpu()
     nfs = SELECT_GROUPS[group]
