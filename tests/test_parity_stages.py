@@ -108,6 +108,8 @@ SELECT_GROUPS = {
     "le64k": [600, 32769, 40000, 65535, 65536],
     "stream": [700, 12500, 65537, 100000, 131072],
     "ms262k": [5, 32769, 131073, 262144],
+    # the longest row the library takes (QSA_MAX_BLOCKS: a 4M-token context)
+    "max4m": [1 << 20, 70001],
 }
 
 
