@@ -5,10 +5,10 @@
 // BF16 queries and BF16 or FP8 E4M3 KV.  This is a gfx950 design for the same
 // contract.
 //
-// Work unit: (query, KV head, split of the position buffer), query fastest in
-// the 1-D grid.  A wave takes
-// 32 gathered positions per step and serves the whole GQA group of that KV
-// head (up to 16 query heads) at once on bf16 MFMA 16x16x32:
+// Work unit: (query, KV head, split of the position buffer), the position in
+// a 3-D grid dispatched query fastest and split slowest.  A wave takes 32
+// gathered positions per step and serves the whole GQA group of that KV head
+// (up to 16 query heads) at once on bf16 MFMA 16x16x32:
 //   S^T[pos][head] = K[pos][:] . Q[head][:]      (2 tiles x 4 MFMAs)
 //   O^T[dim][head] += V^T[dim][pos] P^T[pos][head]  (8 MFMAs each for the BF16
 //                                                    high and low parts of P)
@@ -22,13 +22,14 @@
 // the V scale into the final normalisation.
 //
 // Softmax is online per wave (running reference max, moved lazily, and sum in
-// the log2 domain), the 4
-// waves of a workgroup merge in LDS, and when a unit is split over several
-// workgroups the last one to finish merges the partials (an arrival counter
-// in the workspace, one 128-byte line per unit, reset to zero by that last
-// workgroup).  Partials travel through 16-byte device-scope stores and loads
-// that bypass the per-XCD caches, so the hand-off needs no cache flush or
-// invalidation.
+// the log2 domain), the 4 waves of a workgroup merge in LDS, and when a unit
+// is split over several workgroups the last one to finish merges the
+// partials (an arrival counter in the workspace, one 128-byte line per unit,
+// reset to zero by that last workgroup).  Partials travel through
+// device-scope buffer stores and loads that bypass the per-XCD caches, so the
+// hand-off needs no cache flush or invalidation.  In the large-batch
+// (non-temporal) kernels the K rows of a step go through LDS by
+// direct-to-LDS loads of whole lines; V always goes to registers.
 #include "qsa_common.hpp"
 #include "qsa_launch.hpp"
 
