@@ -137,7 +137,6 @@ template <bool kFp8> struct KLds {
   static constexpr int kRowBytes = kFp8 ? 128 : 256;
   static constexpr int kBytes = 32 * kRowBytes;              // one chunk
   static constexpr int kLoads = kBytes / 1024;               // load instructions per chunk
-  static constexpr int kBufs = kFp8 ? 2 : 1;                 // FP8 double-buffers chunks
   __device__ static constexpr int swz(int r) { return kFp8 ? (r >> 1) & 7 : r & 15; }
 };
 

@@ -94,11 +94,6 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return min(a, b);
 }
 
-__device__ __forceinline__ float fdot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
-                                         c, false);
-}
-
 // Wave-wide inclusive prefix sum of unsigned values: a DPP shift-scan inside
 // each 16-lane row (lanes shifted in from outside the row read 0), then the
 // row totals are added through lane reads.

@@ -9,9 +9,9 @@
 // exact and accumulate in FP32.
 //
 // Step kk of the chain contracts dimensions 32kk .. 32kk+31: lane l = 16g + n
-// of a wave loads bytes 64kk + 16g .. 64kk + 16g + 15 of key row n of the
-// tile, so one load instruction reads 64 contiguous bytes of each of 16 rows.
-// The result leaves lane (g, n) with query n's scores of rows 4g .. 4g+3.
+// of a wave takes bytes 64kk + 16g .. 64kk + 16g + 15 of key row n of the
+// tile (from the wave's LDS copy of it, below) as its A operand.  The result
+// leaves lane (g, n) with query n's scores of rows 4g .. 4g+3.
 #pragma once
 
 #include "qsa_common.hpp"
@@ -23,15 +23,6 @@ constexpr int kKeyRowBytes = QSA_INDEX_DIM * 2;
 struct KeyTile {
   u32x4 w[4];    // step kk: dimensions 32kk + 8g .. 32kk + 8g + 7 of row n
 };
-
-// Loads of the tile starting at key row row0 of the rows behind rs (reads
-// past the descriptor's bound return zeros).
-__device__ __forceinline__ void load_key_tile(KeyTile& t, __amdgpu_buffer_rsrc_t rs, int row0, int n, int g) {
-  const int off = (row0 + n) * kKeyRowBytes + 16 * g;
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    t.w[kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64 * kk, 0, 0));
-}
 
 // The request's index queries as the MFMA B operand: lane (g, n) holds query
 // n's dimensions 32kk + 8g .. + 7 for step kk (zeros for n >= nq).
