@@ -246,6 +246,52 @@ def calibrate_copy(gib: int = 1, reps: int = 3) -> None:
     torch.cuda.empty_cache()
 
 
+def stream_ceiling(gib: int = 1, reps: int = 7) -> dict:
+    """Measured context for the roofline on `gib` GiB of zero-filled device
+    memory: a streaming read (the probe library's whole-line non-temporal
+    read kernel, 4,096 workgroups) and torch's device-to-device copy (bytes
+    read + written per second), each the median of `reps` event-timed runs."""
+    import ctypes
+
+    import torch
+    from block_sparse_attention_qsa_amd.build import PROBE_LIB
+    probe = ctypes.CDLL(PROBE_LIB)
+    probe.qsa_probe_stream_read.restype = ctypes.c_int
+    probe.qsa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int,
+                                            ctypes.c_void_p]
+    src = torch.zeros(gib << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def read():
+        rc = probe.qsa_probe_stream_read(src.data_ptr(), src.numel() * 4, sink.data_ptr(), 4096,
+                                         torch.cuda.current_stream().cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"stream-read probe failed: hipError {rc}")
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+        return sorted(times)[reps // 2]
+
+    nbytes = gib << 30
+    read_gbps = nbytes / timed(read) / 1e9
+    copy_gbps = 2 * nbytes / timed(lambda: dst.copy_(src)) / 1e9
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return {"read_gbps": round(read_gbps, 1), "read_frac_of_peak": round(read_gbps / HBM_PEAK_GBPS, 4),
+            "copy_gbps": round(copy_gbps, 1),
+            "kind": f"streaming read of {gib} GiB (probe kernel); torch copy ({gib} GiB read + {gib} GiB written)"}
+
+
 # ------------------------------------------------------------------ profile summaries
 PROFILE_WORKLOADS = ("mtp50k", "mtp50k_b32_fp8", "mtp1m")
 PROF_STATS_CMD = ("rocprofv3 --kernel-trace --stats -d {d}/stats_{W} -o qsa --output-format csv -- "
@@ -455,6 +501,8 @@ def main():
         if r3["kernels"]:
             line["long"]["roofline"] = roofline_of(r3, traffic)
         del w3
+    if not args.no_kernels:
+        line["stream_ceiling"] = stream_ceiling()
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -18,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqsa.so")
+PROBE_SRC = os.path.join(PKG, "probe", "stream_read.hip")
+PROBE_LIB = os.path.join(PKG, "libqsa_probe.so")   # the benchmark's stream-read ceiling, not the QSA ABI
 ARCH = "gfx950"
 
 
@@ -28,13 +30,12 @@ def hipcc() -> str:
     return exe
 
 
-def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB + f".tmp{os.getpid()}"
+def _compile(srcs, out: str, verbose: bool) -> str:
+    tmp = out + f".tmp{os.getpid()}"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Wall", "-Wno-unused-function",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-           "-I", INCLUDE, "-I", CSRC, "-o", tmp] + srcs
+           "-I", INCLUDE, "-I", CSRC, "-o", tmp] + list(srcs)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,7 +47,14 @@ def build(verbose: bool = False) -> str:
         lines = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l]
         if any(l.strip() for l in lines):
             sys.stderr.write("\n".join(lines) + "\n")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Build libqsa.so and the benchmark's stream-read probe library."""
+    _compile(sorted(glob.glob(os.path.join(CSRC, "*.hip"))), LIB, verbose)
+    _compile([PROBE_SRC], PROBE_LIB, verbose)
     return LIB
 
 

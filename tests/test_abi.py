@@ -107,3 +107,19 @@ def test_python_binding_refuses_host_tensors():
     b = qsa.Batch.__new__(qsa.Batch)
     with pytest.raises(qsa.QsaError):
         qsa._dev(torch.zeros(4, 128, dtype=torch.bfloat16), "idx_q", qsa._BF16)
+
+
+def test_stream_probe_library_loads_and_checks_arguments():
+    """The benchmark's stream-read probe (its roofline context, not part of
+    the QSA ABI) is built beside the library and refuses bad arguments before
+    launching."""
+    from block_sparse_attention_qsa_amd.build import PROBE_LIB
+    if not os.path.exists(PROBE_LIB):
+        pytest.fail(f"{PROBE_LIB} is not built; run the package build")
+    probe = ctypes.CDLL(PROBE_LIB)
+    fn = probe.qsa_probe_stream_read
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    assert fn(None, 1 << 20, ctypes.c_void_p(0x1000), 4096, None) != 0              # no source
+    assert fn(ctypes.c_void_p(0x1004), 1 << 20, ctypes.c_void_p(0x1000), 4096, None) != 0   # misaligned
+    assert fn(ctypes.c_void_p(0x1000), 1 << 20, ctypes.c_void_p(0x1000), 0, None) != 0     # no grid
