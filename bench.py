@@ -184,8 +184,13 @@ def measure(name: str, steps: int, warmup: int, kernels: bool = True) -> dict:
 
 KERNEL_NAMES = {"score": "qsa::score_kernel", "select": "qsa::select_reg_kernel", "attn": "qsa::attn_kernel"}
 # rows over 32,768 blocks take the five-kernel multi-workgroup top-k
-MS_SELECT_NAME = "qsa::ms_*_kernel (5 launches)"
-MS_MIN_BLOCKS = 32768
+LONG_SELECT_NAME = "qsa::select_slice_kernel + qsa::select_cand_kernel (2 launches)"
+LONG_ROW_BLOCKS = 32768
+
+
+def _long_select(kernel: str) -> bool:
+    """One of the two launches of the top-k for rows over 32,768 blocks."""
+    return "select_slice_kernel" in kernel or "select_cand_kernel" in kernel
 CSRC = os.path.join(ROOT, "block_sparse_attention_qsa_amd", "csrc")
 
 
@@ -223,8 +228,8 @@ def roofline_of(res: dict, traffic: dict | None) -> dict:
     k = ks[dom]
     tr = None
     name = KERNEL_NAMES[dom]
-    if dom == "select" and res.get("max_blocks", 0) > MS_MIN_BLOCKS:
-        name = MS_SELECT_NAME
+    if dom == "select" and res.get("max_blocks", 0) > LONG_ROW_BLOCKS:
+        name = LONG_SELECT_NAME
     key = f"{name}@{res['workload']}"
     if traffic and key in traffic.get("entries", {}) and traffic.get("source_sha256") == kernel_source_hash():
         tr = traffic["entries"][key]["bytes_per_launch"]
@@ -306,7 +311,7 @@ def _stage_of(kernel: str):
         return "attn"
     if "score_kernel" in kernel:
         return "score"
-    if "select_reg_kernel" in kernel or "qsa::ms_" in kernel:
+    if "select_reg_kernel" in kernel or _long_select(kernel):
         return "select"
     return None
 
@@ -316,7 +321,7 @@ def summarize_profiles(prof_dir: str, out_dir: str) -> None:
     directory per workload and counter under prof_dir) into one markdown
     summary per workload and traffic.json under out_dir.  The memory counters
     are scaled by what they read for the 1 GiB device copy of --calibrate-copy;
-    the five launches of the multi-workgroup top-k are summed into one entry."""
+    the two launches of the long-row top-k are summed into one entry."""
     import collections
     import csv
     from workloads import make_workload
@@ -377,16 +382,16 @@ def summarize_profiles(prof_dir: str, out_dir: str) -> None:
             fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
             tot = (fk * cf + wk * cw) * 1024
             out.append(f"| `{n}` | {len(fv)} | {fk:.1f} | {wk:.1f} | {tot / 1e6:.3f} | "
-                       f"{alg[st] / 1e6 if 'qsa::ms_' not in n else float('nan'):.3f} | "
-                       f"{tot / alg[st] if 'qsa::ms_' not in n else float('nan'):.3f} |")
-            key = MS_SELECT_NAME if "qsa::ms_" in n else KERNEL_NAMES[st]
+                       f"{alg[st] / 1e6 if not _long_select(n) else float('nan'):.3f} | "
+                       f"{tot / alg[st] if not _long_select(n) else float('nan'):.3f} |")
+            key = LONG_SELECT_NAME if _long_select(n) else KERNEL_NAMES[st]
             acc = summed[key]
             acc[0] += fk
             acc[1] += wk
             acc[2] += tot
         for key, (fk, wk, tot) in summed.items():
-            st = [s for s in KERNEL_NAMES if KERNEL_NAMES[s] == key or (key == MS_SELECT_NAME and s == "select")][0]
-            if key == MS_SELECT_NAME:
+            st = [s for s in KERNEL_NAMES if KERNEL_NAMES[s] == key or (key == LONG_SELECT_NAME and s == "select")][0]
+            if key == LONG_SELECT_NAME:
                 out.append(f"| {key}, summed | | {fk:.1f} | {wk:.1f} | {tot / 1e6:.3f} | {alg[st] / 1e6:.3f} | "
                            f"{tot / alg[st]:.3f} |")
             traffic["entries"][f"{key}@{W}"] = {"bytes_per_launch": int(round(tot)), "fetch_kib": fk,

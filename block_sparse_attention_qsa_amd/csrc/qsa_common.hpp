@@ -140,35 +140,9 @@ __device__ __forceinline__ uint32_t lds_slots_min(const uint32_t* slots, int nw)
   return wave_min_u32(lane_id() < nw ? slots[lane_id()] : 0xFFFFFFFFu);
 }
 
-// Multi-workgroup selection for long rows: each query's row is cut into
-// slices of kMsSlice blocks (kMsE per thread of a kMsNT-thread workgroup).
-// Per-query state lives in the workspace as one record of `stride` words.
-constexpr int kMsNT = 256;
-constexpr int kMsE = 16;
-constexpr int kMsSlice = kMsNT * kMsE;     // 4,096 blocks
-constexpr int kMsCandCap = 256;            // threshold-bin population ranked directly
-constexpr int kMsMinBlocks = 32768;        // rows longer than this take the multi-workgroup path
-
-struct MsLayout {
-  int slices;                               // slices of the longest row
-  int64_t ctrl, part, cnt, off, take, cand, hist, kmap, stride;   // word offsets in a query record
-};
-
-__host__ __device__ inline MsLayout ms_layout(int max_blocks) {
-  MsLayout l;
-  l.slices = max_blocks > 0 ? (max_blocks + kMsSlice - 1) / kMsSlice : 1;
-  int64_t o = 0;                            // ctrl and hist first: hist stays 16-byte aligned
-  l.ctrl = o;  o += 16;
-  l.hist = o;  o += kRadixBins;
-  l.cand = o;  o += 2 * kMsCandCap;
-  l.part = o;  o += 2 * (int64_t)l.slices;
-  l.cnt = o;   o += 2 * (int64_t)l.slices;
-  l.off = o;   o += l.slices;
-  l.take = o;  o += l.slices;
-  l.kmap = o;  o += (int64_t)l.slices * (kMsSlice / 32);
-  l.stride = (o + 63) / 64 * 64;            // 256-byte records
-  return l;
-}
+// Rows longer than this many blocks are selected in two launches (slices,
+// then their candidates); shorter ones by one workgroup per query.
+constexpr int kLongRowBlocks = 32768;
 
 // Attention split geometry shared by the launcher and the workspace sizing.
 struct AttnSplit {

@@ -47,7 +47,8 @@ struct AttnArgs {
 hipError_t launch_score(const Meta& m, const void* idx_q, const void* ckeys, float* scores, int64_t ld,
                         hipStream_t stream);
 // Writes sel/n_sel, and pos/n_pos too when pos != nullptr.  Rows longer than
-// 32,768 blocks use select_workspace_bytes() of workspace at ws (256-byte
+// 32,768 blocks keep their slices' candidates in select_workspace_bytes() of
+// workspace at ws (256-byte
 // aligned; no initial contents needed).
 hipError_t launch_select(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel,
                          int32_t* n_sel, int32_t* pos, int32_t* n_pos, int width, void* ws, hipStream_t stream);

@@ -7,27 +7,25 @@
 // article (first optimisation) adds the last step: locate the kept pieces in
 // the KV cache.
 //
-// Three selectors, chosen by the longest row of the batch:
+// One selector body (select_row), chosen launches by the longest row of the
+// batch:
 //   * rows of up to 32,768 blocks: select_reg_kernel, one workgroup per query
 //     with the whole row in registers (a linear value grid finds the bin of
-//     the k-th best score, its few candidates are ranked exactly);
-//   * longer rows: five multi-workgroup launches over 4,096-block slices that
-//     share the same value grid, with per-query state in caller workspace;
-//   * any row the grid cannot split (no finite range, NaN scores, a crowded
-//     threshold bin) falls back to exact MSB-first radix passes over
-//     order-preserving keys: in registers inside select_reg_kernel, streamed
-//     from the score buffer by select_stream_row behind the multi-workgroup
-//     launches.
-// All three keep every block above the threshold and the lowest-index blocks
-// that tie with it, and write sel (and, fused, pos) in ascending order.
+//     the k-th best score, its few candidates are ranked exactly; any row the
+//     grid cannot split - no finite range, NaN scores, a crowded threshold
+//     bin - falls back to exact MSB-first radix passes over order-preserving
+//     keys);
+//   * longer rows (up to 4M-token contexts): select_slice_kernel keeps the
+//     top k of every 16,384-block slice with the same body, then
+//     select_cand_kernel keeps the top k of those candidates per query.
+// Both keep every block above the threshold and the lowest-index blocks that
+// tie with it, and write sel (and, fused, pos) in ascending order.
 
 #include "qsa_common.hpp"
 #include "qsa_launch.hpp"
 
 namespace qsa {
 
-constexpr int kKeyCap = 32768;   // keys staged in LDS (128 KiB of the 160 KiB a workgroup may use)
-constexpr int kBatch = 8;        // loads a thread keeps in flight while streaming scores
 constexpr int kCandCap = 256;    // threshold-bin population ranked directly
 
 // Inside the fully unrolled per-element loops: a scheduling fence every 4
@@ -170,12 +168,63 @@ __device__ __forceinline__ float wave_min_f32(float v) {
 //      pos.
 // The per-element work of the common path is a bin, two compares and a
 // ballot; only the few candidates take branches.
+// What the selector body reads and writes:
+//   kRowQuery  query q's score row; writes sel / n_sel (and pos / n_pos);
+//   kRowSlice  slice lr.slice (E * NT blocks) of query q's score row; writes
+//              the kept blocks' indices and scores, min(k, slice length) of
+//              them, to the candidate rows at lr.slice * k;
+//   kRowCand   query q's candidate row (every slice's kept blocks, slice by
+//              slice, each in ascending index order); writes sel / n_sel (and
+//              pos / n_pos) for the kept candidates' block indices.
+// A block of the row's top k is in its slice's top k (the order is total),
+// and every slice but the last keeps exactly k, so the candidate row is dense
+// and in ascending block order: the lower-index-wins rule carries over.
+constexpr int kRowQuery = 0, kRowSlice = 1, kRowCand = 2;
+constexpr int kLongSlice = 16384;            // blocks per slice of a long row
+
+struct LongRows {
+  float* cscore;     // [num_q][cstride] candidate scores
+  int32_t* cidx;     // [num_q][cstride] their block indices
+  int cstride;       // candidate row stride: slices * k
+  int slice;         // kRowSlice: the slice this workgroup selects from
+};
+
+// sel / pos rows for the ns kept block indices in sel_s[] (ascending),
+// nf full blocks and a partial block of pl tokens.
+template <int NT, bool kWritePos>
+__device__ __forceinline__ void write_selection(const int32_t* sel_s, int ns, int k, int nf, int pl, const Meta& m,
+                                                int r, int kv0, bool paged, int32_t* __restrict__ sel_row,
+                                                int32_t* __restrict__ pos_row, int width,
+                                                int32_t* __restrict__ n_sel, int32_t* __restrict__ n_pos, int q) {
+  const int tid = threadIdx.x;
+  // the clamp only guards the position buffer against a broken invariant: a
+  // kept index always lies in [0, nf)
+  for (int i = tid; i < k; i += NT) sel_row[i] = i < ns ? min(max(sel_s[i], 0), nf - 1) : -1;
+  if (kWritePos) {
+    const int np = 4 * ns + pl;
+    for (int i = tid; i < width; i += NT) {
+      int v = -1;
+      if (i < 4 * ns) {
+        const int b = min(max(sel_s[i >> 2], 0), nf - 1);
+        v = (paged ? token_slot(m, r, 4 * b) : kv0 + 4 * b) + (i & 3);
+      } else if (i < np) {
+        v = (paged ? token_slot(m, r, 4 * nf) : kv0 + 4 * nf) + (i - 4 * ns);
+      }
+      pos_row[i] = v;
+    }
+  }
+  if (tid == 0) {
+    n_sel[q] = ns;
+    if (kWritePos) n_pos[q] = 4 * ns + pl;
+  }
+}
+
 // The selector body for query q, run by a whole NT-thread workgroup.
-template <int E, int NT, bool kWritePos>
+template <int E, int NT, bool kWritePos, int kRow = kRowQuery>
 __device__ __forceinline__ void select_row(const Meta& m, const float* __restrict__ scores, int64_t ld, int k,
                                            int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
                                            int32_t* __restrict__ pos, int32_t* __restrict__ n_pos, int width,
-                                           const int q) {
+                                           const int q, const LongRows& lr) {
   constexpr int NW = NT / kWave;
   constexpr int ER = E > 32 ? 32 : E;    // scores per thread held in registers
   constexpr int EL = E - ER;             // the rest sit in LDS, column-major
@@ -193,10 +242,15 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   __shared__ uint32_t scan_s[NW];
   __shared__ u32x2 cand_s[kCandCap];
   __shared__ int32_t sel_s[QSA_TOPK];
+  __shared__ float score_s[kRow == kRowSlice ? QSA_TOPK : 1];   // a slice's kept scores
   __shared__ uint32_t s_prefix, s_krem, s_count, s_total, s_ncand;
 
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const float* srow = scores + (int64_t)q * ld;
+  constexpr int S = E * NT;
+  const float* srow = kRow == kRowCand ? lr.cscore + (int64_t)q * lr.cstride
+                                       : scores + (int64_t)q * ld + (kRow == kRowSlice ? (int64_t)lr.slice * S : 0);
+  const int64_t row_ld = kRow == kRowCand ? (int64_t)lr.cstride
+                                          : (kRow == kRowSlice ? ld - (int64_t)lr.slice * S : ld);
 
   // Score loads are issued first, speculatively: thread t owns the fixed segment
   // [t*E, t*E + E), so the loads do not wait for the request metadata.  They
@@ -205,11 +259,11 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   // (slots past the query's block count are discarded afterwards).  With a
   // stride that is a multiple of 4 a 16-byte group never straddles the bound.
   const int beg = tid * E;
-  const uint32_t row_bytes = (uint32_t)min(ld, (int64_t)(1 << 28)) * 4u;
+  const uint32_t row_bytes = (uint32_t)min(max(row_ld, (int64_t)0), (int64_t)(1 << 28)) * 4u;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(srow), 0, (int)row_bytes, 0x00020000);
   float sv[E];
-  if ((ld & 3) == 0) {
+  if (((kRow == kRowCand ? (int64_t)lr.cstride : ld) & 3) == 0) {
 #pragma unroll
     for (int v = 0; v < E / 4; ++v) {
       const f32x4 x =
@@ -233,15 +287,44 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   const int qs = m.q_start[r];
   const int nq = m.q_start[r + 1] - qs;
   const int L = m.seq_len[r] - nq + 1 + (q - qs);
-  int nf = L >> 2;
-  if (nf > m.max_blocks) nf = m.max_blocks;
-  if (nf > E * NT) nf = E * NT;                      // launcher picks E * NT >= max_blocks
+  int nfq = L >> 2;                                  // the query's full blocks
+  if (nfq > m.max_blocks) nfq = m.max_blocks;
+  int nf;                                            // blocks of the row selected from here
+  if (kRow == kRowQuery) {
+    nf = min(nfq, S);                                // launcher picks E * NT >= max_blocks
+    nfq = nf;
+  } else if (kRow == kRowSlice) {
+    nf = max(0, min(S, nfq - lr.slice * S));
+  } else {
+    const int P = (nfq + kLongSlice - 1) / kLongSlice;
+    nf = P <= 1 ? min(k, nfq) : (P - 1) * k + min(k, nfq - (P - 1) * kLongSlice);
+    nf = min(nf, S);
+  }
   const int pl = L & 3;
   const bool paged = m.page_table != nullptr;
   const int kv0 = paged ? 0 : m.kv_start[r];
-  int32_t* sel_row = sel + (int64_t)q * k;
+  int32_t* sel_row = kRow == kRowSlice ? nullptr : sel + (int64_t)q * k;
   int32_t* pos_row = kWritePos ? pos + (int64_t)q * width : nullptr;
+  const int32_t* cidx_row = kRow == kRowCand ? lr.cidx + (int64_t)q * lr.cstride : nullptr;
+  float* cs_out = kRow == kRowSlice ? lr.cscore + (int64_t)q * lr.cstride + (int64_t)lr.slice * k : nullptr;
+  int32_t* ci_out = kRow == kRowSlice ? lr.cidx + (int64_t)q * lr.cstride + (int64_t)lr.slice * k : nullptr;
 
+  if (kRow == kRowSlice && nf <= k) {                // the whole slice is kept
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (beg + e < nf) {
+        cs_out[beg + e] = sv[e];
+        ci_out[beg + e] = lr.slice * S + beg + e;
+      }
+    return;
+  }
+  if (kRow == kRowCand && nf <= k) {                 // every candidate is kept
+    for (int i = tid; i < nf; i += NT) sel_s[i] = cidx_row[i];
+    __syncthreads();
+    write_selection<NT, kWritePos>(sel_s, nf, k, nfq, pl, m, r, kv0, paged, sel_row, pos_row, width, n_sel, n_pos,
+                                   q);
+    return;
+  }
   if (nf <= k) {
     for (int i = tid; i < k; i += NT) sel_row[i] = i < nf ? i : -1;
     if (kWritePos) {
@@ -517,32 +600,27 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
     while (t != 0u) {
       const int e = 32 * i + __builtin_ctz(t);
       t &= t - 1u;
-      if (o < (uint32_t)k) sel_s[o] = beg + e;
+      if (o < (uint32_t)k) {
+        sel_s[o] = beg + e;
+        if (kRow == kRowSlice) score_s[o] = QSA_X(e);
+      }
       ++o;
     }
   }
   const int ns = (int)min((tot >> 20) + min(tot & 0xFFFFFu, need), (uint32_t)k);
   __syncthreads();
-  // the clamp only guards the position buffer against a broken invariant: a
-  // kept index always lies in [0, nf)
-  for (int i = tid; i < k; i += NT) sel_row[i] = i < ns ? min(max(sel_s[i], 0), nf - 1) : -1;
-  if (kWritePos) {
-    const int np = 4 * ns + pl;
-    for (int i = tid; i < width; i += NT) {
-      int v = -1;
-      if (i < 4 * ns) {
-        const int b = min(max(sel_s[i >> 2], 0), nf - 1);
-        v = (paged ? token_slot(m, r, 4 * b) : kv0 + 4 * b) + (i & 3);
-      } else if (i < np) {
-        v = (paged ? token_slot(m, r, 4 * nf) : kv0 + 4 * nf) + (i - 4 * ns);
-      }
-      pos_row[i] = v;
+  if (kRow == kRowSlice) {
+    for (int i = tid; i < ns; i += NT) {
+      cs_out[i] = score_s[i];
+      ci_out[i] = lr.slice * S + sel_s[i];
     }
+    return;
   }
-  if (tid == 0) {
-    n_sel[q] = ns;
-    if (kWritePos) n_pos[q] = 4 * ns + pl;
+  if (kRow == kRowCand) {
+    for (int i = tid; i < ns; i += NT) sel_s[i] = cidx_row[sel_s[i]];   // candidate -> block index
+    __syncthreads();
   }
+  write_selection<NT, kWritePos>(sel_s, ns, k, nfq, pl, m, r, kv0, paged, sel_row, pos_row, width, n_sel, n_pos, q);
 }
 #undef QSA_X
 
@@ -551,645 +629,35 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(Meta m, const float* __r
                                                         int k, int32_t* __restrict__ sel,
                                                         int32_t* __restrict__ n_sel, int32_t* __restrict__ pos,
                                                         int32_t* __restrict__ n_pos, int width) {
-  select_row<E, NT, kWritePos>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, (int)blockIdx.x);
+  select_row<E, NT, kWritePos>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, (int)blockIdx.x, LongRows{});
 }
 
-// Exact selection of one query's row by a whole 1024-thread workgroup (any
-// row length, any scores): the body of select_stream_kernel, also the
-// fallback of the multi-workgroup selector.
-template <bool kWritePos>
-__device__ void select_stream_row(Meta m, const float* __restrict__ scores, int64_t ld, int k,
-                                  int32_t* __restrict__ sel, int32_t* __restrict__ n_sel, int32_t* __restrict__ pos,
-                                  int32_t* __restrict__ n_pos, int width, int q) {
-  constexpr int NT = kSelectThreads;
-  __shared__ uint32_t keys_lds[kKeyCap];
-  __shared__ uint32_t hist[kRadixBins];
-  __shared__ uint32_t scan_scratch[NT / kWave];
-  __shared__ uint32_t s_prefix, s_krem, s_count, s_ncand;
-
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  const int r = request_of(m.q_start, m.num_req, q);
-  const int qs = m.q_start[r];
-  const int nq = m.q_start[r + 1] - qs;
-  const int L = m.seq_len[r] - nq + 1 + (q - qs);
-  int nf = L >> 2;
-  if (nf > m.max_blocks) nf = m.max_blocks;
-  const int pl = L & 3;
-  const bool paged = m.page_table != nullptr;
-  const int kv0 = paged ? 0 : m.kv_start[r];
-  const float* srow = scores + (int64_t)q * ld;
-  int32_t* sel_row = sel + (int64_t)q * k;
-  int32_t* pos_row = kWritePos ? pos + (int64_t)q * width : nullptr;
-
-  if (nf <= k) {
-    // every full block is kept: positions are simply the causal prefix
-    for (int i = tid; i < k; i += NT) sel_row[i] = i < nf ? i : -1;
-    if (kWritePos) {
-      const int np = 4 * nf + pl;
-      for (int i = tid; i < width; i += NT) pos_row[i] = i < np ? (paged ? token_slot(m, r, i) : kv0 + i) : -1;
-    }
-    if (tid == 0) {
-      n_sel[q] = nf;
-      if (kWritePos) n_pos[q] = 4 * nf + pl;
-    }
-    return;
-  }
-
-  // ---- 1. keys.  All nf keys go to LDS when they fit; otherwise the first
-  // radix pass streams the score buffer and only the keys of the chosen
-  // top-level bin are staged for the later passes.
-  const bool staged = nf <= kKeyCap;
-  if (staged) {
-#pragma unroll
-    for (int b = 0; b < kKeyCap / NT; b += kBatch) {
-      float v[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int i = (b + u) * NT + tid;
-        v[u] = i < nf ? srow[i] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int i = (b + u) * NT + tid;
-        if (i < nf) keys_lds[i] = score_key(v[u]);
-      }
-    }
-  }
-
-  // ---- 2. MSB-first radix passes over 11, 11 and 10 bits.
-  int nkeys = staged ? nf : 0;
-  bool from_lds = staged;
-  uint32_t prefix = 0u, pmask = 0u, krem = (uint32_t)k;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
-    for (int i = tid; i < kRadixBins; i += NT) hist[i] = 0u;
-    __syncthreads();
-    if (from_lds) {
-      for (int i0 = 0; i0 < nkeys; i0 += NT) {
-        const int i = i0 + tid;
-        const uint32_t key = i < nkeys ? keys_lds[i] : 0u;
-        hist_add(hist, (key >> shift) & dmask, i < nkeys && (key & pmask) == prefix);
-      }
-    } else {
-      for (int base = 0; base < nf; base += NT * kBatch) {
-        float v[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int i = base + u * NT + tid;
-          v[u] = i < nf ? srow[i] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int i = base + u * NT + tid;
-          const uint32_t key = score_key(v[u]);
-          hist_add(hist, (key >> shift) & dmask, i < nf && (key & pmask) == prefix);
-        }
-      }
-    }
-    __syncthreads();
-    if (wave == 0) find_bucket(hist, krem, prefix, shift, &s_prefix, &s_krem, &s_count);
-    if (tid == 0) s_ncand = 0u;
-    __syncthreads();
-    // every thread reads the shared results of this pass before any thread can
-    // reach the next pass (which clears hist and rewrites them after a barrier)
-    prefix = s_prefix;
-    krem = s_krem;
-    const uint32_t bin_count = s_count;
-    pmask |= dmask << shift;
-    if (!from_lds && bin_count <= (uint32_t)kKeyCap) {
-      // stage the keys of the chosen top-level bin (wave-aggregated append)
-      for (int base = 0; base < nf; base += NT * kBatch) {
-        float v[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int i = base + u * NT + tid;
-          v[u] = i < nf ? srow[i] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int i = base + u * NT + tid;
-          const uint32_t key = score_key(v[u]);
-          const bool mine = i < nf && (key & pmask) == prefix;
-          const uint64_t bal = __ballot(mine);
-          if (bal) {
-            uint32_t wbase = 0;
-            if (lane == 0) wbase = atomicAdd(&s_ncand, (uint32_t)__popcll(bal));
-            wbase = (uint32_t)__builtin_amdgcn_readfirstlane((int)wbase);
-            const uint32_t rank =
-                __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            if (mine) keys_lds[wbase + rank] = key;
-          }
-        }
-      }
-      __syncthreads();
-      nkeys = (int)s_ncand;
-      from_lds = true;
-    }
-  }
-  const uint32_t T = prefix;        // key of the k-th best block
-  const uint32_t need_eq = krem;    // blocks equal to T that are kept (lowest indices first)
-
-  // ---- 3. ordered compaction over contiguous per-thread segments [beg, end):
-  // one packed scan gives, before this thread, the count of keys > T (high
-  // 12 bits) and of keys == T (low 20 bits); the kept keys before it are
-  // gt_before + min(eq_before, need_eq).
-  const int E = (nf + NT - 1) / NT;
-  const int beg = min(tid * E, nf), end = min(beg + E, nf);
-  uint32_t gt = 0, eq = 0;
-  for (int i0 = beg; i0 < end; i0 += kBatch) {
-    uint32_t kk[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + u;
-      kk[u] = i < end ? (staged ? keys_lds[i] : score_key(srow[i])) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      gt += (i0 + u < end) && kk[u] > T;
-      eq += (i0 + u < end) && kk[u] == T;
-    }
-  }
-  uint32_t tot;
-  const uint32_t before = block_exclusive_scan<NT>((gt << 20) | eq, scan_scratch, &tot);
-  const uint32_t eq_before = before & 0xFFFFFu;
-  uint32_t o = (before >> 20) + min(eq_before, need_eq);
-  uint32_t seen = eq_before;
-  for (int i0 = beg; i0 < end; i0 += kBatch) {
-    uint32_t kk[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + u;
-      kk[u] = i < end ? (staged ? keys_lds[i] : score_key(srow[i])) : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + u;
-      bool take = false;
-      if (i < end) {
-        take = kk[u] > T;
-        if (kk[u] == T) {
-          take = seen < need_eq;
-          ++seen;
-        }
-      }
-      if (take) {
-        sel_row[o] = i;
-        if (kWritePos) {
-          const int p0 = paged ? token_slot(m, r, 4 * i) : kv0 + 4 * i;
-          pos_row[4 * o + 0] = p0;
-          pos_row[4 * o + 1] = p0 + 1;
-          pos_row[4 * o + 2] = p0 + 2;
-          pos_row[4 * o + 3] = p0 + 3;
-        }
-        ++o;
-      }
-    }
-  }
-  if (kWritePos) {
-    for (int i = 4 * k + tid; i < width; i += NT) {
-      const int t = i - 4 * k;
-      pos_row[i] = t < pl ? (paged ? token_slot(m, r, 4 * nf) : kv0 + 4 * nf) + t : -1;
-    }
-  }
-  if (tid == 0) {
-    n_sel[q] = k;
-    if (kWritePos) n_pos[q] = 4 * k + pl;
-  }
+// Long rows, launch 1: grid (query, slice); each workgroup keeps the top k
+// of one 16,384-block slice of its query's row.
+__global__ __launch_bounds__(kSelectThreads) void select_slice_kernel(Meta m, const float* __restrict__ scores,
+                                                                      int64_t ld, int k, LongRows lr) {
+  lr.slice = (int)blockIdx.y;
+  select_row<kLongSlice / kSelectThreads, kSelectThreads, false, kRowSlice>(m, scores, ld, k, nullptr, nullptr,
+                                                                             nullptr, nullptr, 0,
+                                                                             (int)blockIdx.x, lr);
 }
 
-// ---------------------------------------------------------------------------
-// Multi-workgroup selection for rows longer than kMsMinBlocks blocks (up to
-// 1M-token contexts).  A row is cut into slices of 4,096 blocks; five
-// launches, with no workgroup ever waiting on another:
-//   1. range     each slice's smallest and largest key; per-query state reset
-//   2. histogram each slice bins its scores on the row's linear grid (the same
-//                monotone map as the single-workgroup selector) into a global
-//                per-query histogram
-//   3. classify  every slice finds the threshold bin B0 from the histogram,
-//                counts its blocks above B0 and inside it, and stages the
-//                candidates (or their key range when there are many)
-//   4. resolve   one workgroup per query ranks the candidates (kept ones go to
-//                a bitmap), or keeps B0 whole, or keeps the lowest-index ties
-//                when B0 holds one key, and gives every slice its output
-//                offset; any other row (no finite range, NaN, a crowded B0
-//                of several keys) is selected exactly by the streaming
-//                selector in this same workgroup
-//   5. write     every slice writes its kept block indices and positions at
-//                its offset.
-
-__device__ __forceinline__ int query_full_blocks(const Meta& m, int q, int* r_out, int* pl_out) {
-  const int r = request_of(m.q_start, m.num_req, q);
-  const int qs = m.q_start[r];
-  const int nq = m.q_start[r + 1] - qs;
-  const int L = m.seq_len[r] - nq + 1 + (q - qs);
-  int nf = L >> 2;
-  if (nf > m.max_blocks) nf = m.max_blocks;
-  *r_out = r;
-  *pl_out = L & 3;
-  return nf;
-}
-
-// Loads this thread's kMsE scores of slice p (beg = first block); reads past
-// the row stride return 0, blocks at or past nf become NaN (no grid bin).
-__device__ __forceinline__ void ms_load(const float* srow, int64_t ld, int beg, int nf, float (&x)[kMsE]) {
-  const uint32_t row_bytes = (uint32_t)min(ld, (int64_t)(1 << 28)) * 4u;
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(srow), 0, (int)row_bytes, 0x00020000);
-  if ((ld & 3) == 0) {
-#pragma unroll
-    for (int v = 0; v < kMsE / 4; ++v) {
-      const f32x4 t = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (beg + 4 * v) * 4, 0, 0));
-      x[4 * v] = t.x;
-      x[4 * v + 1] = t.y;
-      x[4 * v + 2] = t.z;
-      x[4 * v + 3] = t.w;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < kMsE; ++e)
-      x[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (beg + e) * 4, 0, 0));
-  }
-  const int cnt = max(0, min(kMsE, nf - beg));
-#pragma unroll
-  for (int e = 0; e < kMsE; ++e) x[e] = e < cnt ? x[e] : __builtin_nanf("");
-}
-
-// Block-wide sum / max / min of one value per thread (NT threads); scratch
-// holds 2 * NT / 64 words; uniform result.  Two barriers.
-template <int NT>
-__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* scratch) {
-  uint32_t tot;
-  (void)block_exclusive_scan<NT>(v, scratch, &tot);
-  __syncthreads();
-  return tot;
-}
-template <int NT>
-__device__ __forceinline__ void block_minmax_u32(uint32_t& mn, uint32_t& mx, uint32_t* scratch) {
-  constexpr int NW = NT / kWave;
-  mn = wave_min_u32(mn);
-  mx = wave_max_u32(mx);
-  const int wave = threadIdx.x / kWave;
-  if (lane_id() == 0) {
-    scratch[wave] = mn;
-    scratch[NW + wave] = mx;
-  }
-  __syncthreads();
-  mn = lds_slots_min(scratch, NW);
-  mx = lds_slots_max(scratch + NW, NW);
-  __syncthreads();
-}
-
-// The row's key range from the slices' partial ranges (slices 0..P-1; P <= NT).
-template <int NT>
-__device__ __forceinline__ void ms_row_range(const uint32_t* rec, const MsLayout& l, int P, uint32_t& kmin,
-                                             uint32_t& kmax, uint32_t* scratch) {
-  kmin = 0xFFFFFFFFu;
-  kmax = 0u;
-  for (int i = threadIdx.x; i < P; i += NT) {
-    kmin = min(kmin, rec[l.part + 2 * i]);
-    kmax = max(kmax, rec[l.part + 2 * i + 1]);
-  }
-  block_minmax_u32<NT>(kmin, kmax, scratch);
-}
-
-// Linear grid over [key_value(kmin), key_value(kmax)], if both are finite and differ.
-__device__ __forceinline__ bool ms_grid(uint32_t kmin, uint32_t kmax, float& lo, float& inv) {
-  lo = key_value(kmin);
-  const float hi = key_value(kmax);
-  const float span = hi - lo;
-  inv = (float)kRadixBins / span;
-  return __builtin_isfinite(lo) && __builtin_isfinite(hi) && span > 0.f && __builtin_isfinite(inv) && inv > 0.f;
-}
-
-__global__ __launch_bounds__(kMsNT) void ms_range_kernel(Meta m, const float* __restrict__ scores, int64_t ld,
-                                                         uint32_t* __restrict__ ws, MsLayout l) {
-  __shared__ uint32_t scratch[2 * kMsNT / kWave];
-  const int q = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
-  uint32_t* rec = ws + (int64_t)q * l.stride;
-  if (p == 0) {
-    for (int i = tid; i < kRadixBins; i += kMsNT) rec[l.hist + i] = 0u;
-    if (tid < 16) rec[l.ctrl + tid] = tid == 1 ? 0xFFFFFFFFu : 0u;
-  }
-  if (tid < kMsSlice / 32) rec[l.kmap + (int64_t)p * (kMsSlice / 32) + tid] = 0u;
-  int r, pl;
-  const int nf = query_full_blocks(m, q, &r, &pl);
-  const int beg = p * kMsSlice + tid * kMsE;
-  float x[kMsE];
-  ms_load(scores + (int64_t)q * ld, ld, beg, nf, x);
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-  for (int e = 0; e < kMsE; ++e) {
-    if (x[e] == x[e]) {           // NaN marks the blocks past the row
-      const uint32_t key = score_key(x[e]);
-      kmin = min(kmin, key);
-      kmax = max(kmax, key);
-    }
-  }
-  // a real NaN score (it drops out above) shows up as a missing histogram entry later
-  block_minmax_u32<kMsNT>(kmin, kmax, scratch);
-  if (tid == 0) {
-    rec[l.part + 2 * p] = kmin;
-    rec[l.part + 2 * p + 1] = kmax;
-  }
-}
-
-__global__ __launch_bounds__(kMsNT) void ms_hist_kernel(Meta m, const float* __restrict__ scores, int64_t ld,
-                                                        int k, uint32_t* __restrict__ ws, MsLayout l) {
-  __shared__ uint32_t lh[kRadixBins];
-  __shared__ uint32_t scratch[2 * kMsNT / kWave];
-  const int q = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
-  uint32_t* rec = ws + (int64_t)q * l.stride;
-  int r, pl;
-  const int nf = query_full_blocks(m, q, &r, &pl);
-  const int P = (nf + kMsSlice - 1) / kMsSlice;
-  if (nf <= k || p >= P) return;
-  uint32_t kmin, kmax;
-  ms_row_range<kMsNT>(rec, l, P, kmin, kmax, scratch);
-  float lo, inv;
-  if (!ms_grid(kmin, kmax, lo, inv)) return;
-  for (int i = tid; i < kRadixBins; i += kMsNT) lh[i] = 0u;
-  float x[kMsE];
-  ms_load(scores + (int64_t)q * ld, ld, p * kMsSlice + tid * kMsE, nf, x);
-  __syncthreads();
-#pragma unroll
-  for (int e = 0; e < kMsE; ++e) {
-    const int b = grid_bin(x[e], lo, inv);
-    if (b >= 0) atomicAdd(&lh[b], 1u);
-  }
-  __syncthreads();
-  for (int i = tid; i < kRadixBins; i += kMsNT)
-    if (lh[i] != 0u) atomicAdd(&rec[l.hist + i], lh[i]);
-}
-
-__global__ __launch_bounds__(kMsNT) void ms_classify_kernel(Meta m, const float* __restrict__ scores, int64_t ld,
-                                                            int k, uint32_t* __restrict__ ws, MsLayout l) {
-  __shared__ uint32_t scratch[2 * kMsNT / kWave];
-  __shared__ uint32_t s_prefix, s_krem, s_count, s_total;
-  const int q = blockIdx.x, p = blockIdx.y, tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  uint32_t* rec = ws + (int64_t)q * l.stride;
-  int r, pl;
-  const int nf = query_full_blocks(m, q, &r, &pl);
-  const int P = (nf + kMsSlice - 1) / kMsSlice;
-  if (nf <= k || p >= P) return;
-  uint32_t kmin, kmax;
-  ms_row_range<kMsNT>(rec, l, P, kmin, kmax, scratch);
-  float lo, inv;
-  if (!ms_grid(kmin, kmax, lo, inv)) return;
-  if (wave == 0) find_bucket(rec + l.hist, (uint32_t)k, 0u, 0, &s_prefix, &s_krem, &s_count, &s_total);
-  __syncthreads();
-  if (s_total != (uint32_t)nf) return;        // a NaN score: the resolve step falls back
-  const int B0 = (int)s_prefix;
-  const uint32_t krem = s_krem, c0 = s_count;
-  const bool ranked = krem != c0 && c0 <= (uint32_t)kMsCandCap;
-  const int beg = p * kMsSlice + tid * kMsE;
-  float x[kMsE];
-  ms_load(scores + (int64_t)q * ld, ld, beg, nf, x);
-  uint32_t nabove = 0u, ninb = 0u, cmin = 0xFFFFFFFFu, cmax = 0u;
-#pragma unroll
-  for (int e = 0; e < kMsE; ++e) {
-    const int b = grid_bin(x[e], lo, inv);
-    nabove += b > B0;
-    const bool mine = b == B0;
-    ninb += mine;
-    if (ranked) {
-      const uint64_t bal = __ballot(mine);
-      if (bal) {
-        uint32_t wbase = 0;
-        if (lane == __builtin_ctzll(bal)) wbase = atomicAdd(&rec[l.ctrl + 0], (uint32_t)__popcll(bal));
-        wbase = (uint32_t)__builtin_amdgcn_readlane((int)wbase, __builtin_ctzll(bal));
-        const uint32_t slot =
-            __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-        if (mine && wbase + slot < (uint32_t)kMsCandCap) {
-          rec[l.cand + 2 * (wbase + slot)] = score_key(x[e]);
-          rec[l.cand + 2 * (wbase + slot) + 1] = (uint32_t)(beg + e);
-        }
-      }
-    } else if (mine) {
-      const uint32_t key = score_key(x[e]);
-      cmin = min(cmin, key);
-      cmax = max(cmax, key);
-    }
-  }
-  if (!ranked && krem != c0) {
-    block_minmax_u32<kMsNT>(cmin, cmax, scratch);
-    if (tid == 0 && cmin <= cmax) {
-      atomicMin(&rec[l.ctrl + 1], cmin);
-      atomicMax(&rec[l.ctrl + 2], cmax);
-    }
-  }
-  const uint32_t sa = block_sum_u32<kMsNT>(nabove, scratch);
-  const uint32_t si = block_sum_u32<kMsNT>(ninb, scratch);
-  if (tid == 0) {
-    rec[l.cnt + 2 * p] = sa;
-    rec[l.cnt + 2 * p + 1] = si;
-  }
-}
-
-enum { kMsFallback = 0, kMsTakeAll = 1, kMsRank = 2, kMsTies = 3 };
-
-template <bool kWritePos>
-__global__ __launch_bounds__(kSelectThreads) void ms_resolve_kernel(Meta m, const float* __restrict__ scores,
-                                                                    int64_t ld, int k, int32_t* __restrict__ sel,
-                                                                    int32_t* __restrict__ n_sel,
-                                                                    int32_t* __restrict__ pos,
-                                                                    int32_t* __restrict__ n_pos, int width,
-                                                                    uint32_t* __restrict__ ws, MsLayout l) {
-  constexpr int NT = kSelectThreads;
-  __shared__ uint32_t scratch[2 * NT / kWave];
-  __shared__ uint32_t scan2[NT / kWave];
-  __shared__ u32x2 cand_s[kMsCandCap];
-  __shared__ uint32_t kept_s[NT];                 // kept candidates per slice (P <= 256)
-  __shared__ uint32_t s_prefix, s_krem, s_count, s_total;
-  const int q = blockIdx.x, tid = threadIdx.x, wave = tid / kWave;
-  uint32_t* rec = ws + (int64_t)q * l.stride;
-  int r, pl;
-  const int nf = query_full_blocks(m, q, &r, &pl);
-  const bool paged = m.page_table != nullptr;
-  const int kv0 = paged ? 0 : m.kv_start[r];
-  int32_t* sel_row = sel + (int64_t)q * k;
-  int32_t* pos_row = kWritePos ? pos + (int64_t)q * width : nullptr;
-  if (nf <= k) {
-    // every full block is kept; the write step has nothing to do for this row
-    for (int i = tid; i < k; i += NT) sel_row[i] = i < nf ? i : -1;
-    if (kWritePos) {
-      const int np = 4 * nf + pl;
-      for (int i = tid; i < width; i += NT) pos_row[i] = i < np ? (paged ? token_slot(m, r, i) : kv0 + i) : -1;
-    }
-    if (tid == 0) {
-      n_sel[q] = nf;
-      if (kWritePos) n_pos[q] = 4 * nf + pl;
-      rec[l.ctrl + 3] = kMsFallback;
-    }
-    return;
-  }
-  const int P = (nf + kMsSlice - 1) / kMsSlice;
-  uint32_t kmin, kmax;
-  ms_row_range<NT>(rec, l, P, kmin, kmax, scratch);
-  float lo, inv;
-  bool grid = ms_grid(kmin, kmax, lo, inv);
-  int B0 = 0;
-  uint32_t krem = 0u, c0 = 0u;
-  if (grid) {
-    if (wave == 0) find_bucket(rec + l.hist, (uint32_t)k, 0u, 0, &s_prefix, &s_krem, &s_count, &s_total);
-    __syncthreads();
-    grid = s_total == (uint32_t)nf;
-    B0 = (int)s_prefix;
-    krem = s_krem;
-    c0 = s_count;
-  }
-  int mode = kMsFallback;
-  if (grid) {
-    if (krem == c0) mode = kMsTakeAll;
-    else if (c0 <= (uint32_t)kMsCandCap) mode = kMsRank;
-    else if (rec[l.ctrl + 1] == rec[l.ctrl + 2]) mode = kMsTies;
-  }
-  if (mode == kMsFallback) {
-    if (tid == 0) rec[l.ctrl + 3] = kMsFallback;
-    select_stream_row<kWritePos>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, q);
-    return;
-  }
-  // kept blocks per slice: above B0, plus the candidates each mode keeps
-  const uint32_t na = tid < P ? rec[l.cnt + 2 * tid] : 0u;
-  const uint32_t ni = tid < P ? rec[l.cnt + 2 * tid + 1] : 0u;
-  uint32_t kept = 0u, take = 0u;
-  if (mode == kMsTakeAll) {
-    kept = na + ni;
-  } else if (mode == kMsRank) {
-    // the staged candidates (exactly c0 of them; the min only guards the buffer)
-    const int nc = (int)min(c0, rec[l.ctrl + 0]);
-    kept_s[tid] = 0u;
-    if (tid < nc) cand_s[tid] = u32x2{rec[l.cand + 2 * tid], rec[l.cand + 2 * tid + 1]};
-    __syncthreads();
-    if (tid < nc) {
-      const u32x2 me = cand_s[tid];
-      uint32_t ahead = 0u;
-      for (int j = 0; j < nc; ++j) {
-        const u32x2 o = cand_s[j];
-        ahead += (o.x > me.x) | ((o.x == me.x) & (o.y < me.y));
-      }
-      if (ahead < krem && me.y < (uint32_t)nf) {
-        atomicOr(&rec[l.kmap + (me.y >> 5)], 1u << (me.y & 31));
-        atomicAdd(&kept_s[me.y / kMsSlice], 1u);
-      }
-    }
-    __syncthreads();
-    kept = na + kept_s[tid];
-  } else {   // kMsTies: B0 holds one key; the lowest-index krem of its blocks are kept
-    uint32_t tot_ties;
-    const uint32_t tie_before = block_exclusive_scan<NT>(ni, scan2, &tot_ties);
-    take = min(krem - min(tie_before, krem), ni);   // written without a conditional subtraction
-    kept = na + take;
-    __syncthreads();
-  }
-  uint32_t total;
-  const uint32_t off = block_exclusive_scan<NT>(kept, scratch, &total);
-  if (tid < P) {
-    rec[l.off + tid] = off;
-    rec[l.take + tid] = take;
-  }
-  if (tid == 0) {
-    rec[l.ctrl + 3] = (uint32_t)mode;
-    rec[l.ctrl + 4] = __float_as_uint(lo);
-    rec[l.ctrl + 5] = __float_as_uint(inv);
-    rec[l.ctrl + 6] = (uint32_t)B0;
-    n_sel[q] = k;
-    if (kWritePos) n_pos[q] = 4 * k + pl;
-  }
-  if (kWritePos) {
-    for (int i = 4 * k + tid; i < width; i += NT) {
-      const int t = i - 4 * k;
-      pos_row[i] = t < pl ? (paged ? token_slot(m, r, 4 * nf) : kv0 + 4 * nf) + t : -1;
-    }
-  }
-}
-
-template <bool kWritePos>
-__global__ __launch_bounds__(kMsNT) void ms_write_kernel(Meta m, const float* __restrict__ scores, int64_t ld,
-                                                         int k, int32_t* __restrict__ sel,
-                                                         int32_t* __restrict__ pos, int width,
-                                                         const uint32_t* __restrict__ ws, MsLayout l) {
-  __shared__ uint32_t scan1[kMsNT / kWave], scan2[kMsNT / kWave];
-  const int q = blockIdx.x, p = blockIdx.y, tid = threadIdx.x;
-  const uint32_t* rec = ws + (int64_t)q * l.stride;
-  int r, pl;
-  const int nf = query_full_blocks(m, q, &r, &pl);
-  const int P = (nf + kMsSlice - 1) / kMsSlice;
-  if (nf <= k || p >= P) return;
-  const int mode = (int)rec[l.ctrl + 3];
-  if (mode == kMsFallback) return;
-  const float lo = __uint_as_float(rec[l.ctrl + 4]), inv = __uint_as_float(rec[l.ctrl + 5]);
-  const int B0 = (int)rec[l.ctrl + 6];
-  const int beg = p * kMsSlice + tid * kMsE;
-  float x[kMsE];
-  ms_load(scores + (int64_t)q * ld, ld, beg, nf, x);
-  ElemBits<kMsE> above, inb;
-  above.clear();
-  inb.clear();
-#pragma unroll
-  for (int e = kMsE - 1; e >= 0; --e) {
-    const int b = grid_bin(x[e], lo, inv);
-    above.push(e, b > B0);
-    inb.push(e, b == B0);
-  }
-  uint32_t keep = above.w[0];
-  if (mode == kMsTakeAll) {
-    keep |= inb.w[0];
-  } else if (mode == kMsRank) {
-    const uint32_t word = rec[l.kmap + (beg >> 5)] >> (beg & 31);
-    keep |= inb.w[0] & word & ((1u << kMsE) - 1u);
-  }
-  // the ties mode: this thread keeps the lowest of its ties that the slice's quota still allows
-  uint32_t tt;
-  const uint32_t tb = block_exclusive_scan<kMsNT>(__popc(inb.w[0]), scan1, &tt);
-  if (mode == kMsTies) {
-    const uint32_t quota = rec[l.take + p];
-    uint32_t mine = min(quota - min(tb, quota), (uint32_t)__popc(inb.w[0]));
-    uint32_t t = inb.w[0];
-    while (mine != 0u && t != 0u) {
-      const uint32_t low = t & (0u - t);
-      keep |= low;
-      t ^= low;
-      --mine;
-    }
-  }
-  uint32_t tk;
-  uint32_t o = rec[l.off + p] + block_exclusive_scan<kMsNT>(__popc(keep), scan2, &tk);
-  const bool paged = m.page_table != nullptr;
-  const int kv0 = paged ? 0 : m.kv_start[r];
-  int32_t* sel_row = sel + (int64_t)q * k;
-  int32_t* pos_row = kWritePos ? pos + (int64_t)q * width : nullptr;
-  while (keep != 0u) {
-    const int i = beg + __builtin_ctz(keep);
-    keep &= keep - 1u;
-    if (o < (uint32_t)k) {
-      sel_row[o] = i;
-      if (kWritePos) {
-        const int s0 = paged ? token_slot(m, r, 4 * i) : kv0 + 4 * i;
-        pos_row[4 * o + 0] = s0;
-        pos_row[4 * o + 1] = s0 + 1;
-        pos_row[4 * o + 2] = s0 + 2;
-        pos_row[4 * o + 3] = s0 + 3;
-      }
-    }
-    ++o;
-  }
+// Long rows, launch 2: one workgroup per query keeps the top k of the
+// query's candidate row and writes sel (and pos).
+template <int E, bool kWritePos>
+__global__ __launch_bounds__(kSelectThreads) void select_cand_kernel(Meta m, int k, int32_t* __restrict__ sel,
+                                                                     int32_t* __restrict__ n_sel,
+                                                                     int32_t* __restrict__ pos,
+                                                                     int32_t* __restrict__ n_pos, int width,
+                                                                     LongRows lr) {
+  select_row<E, kSelectThreads, kWritePos, kRowCand>(m, nullptr, 0, k, sel, n_sel, pos, n_pos, width,
+                                                      (int)blockIdx.x, lr);
 }
 
 // Position buffer from a selection: of the first min(n_sel, k) entries of
 // the (ascending) selection row, those below nf are used; later ones are not
 // full blocks of this query and are dropped, so that a selection made for a
 // longer query can be reused.
-template <bool kWritePos>
-__global__ __launch_bounds__(kSelectThreads) void select_stream_kernel(Meta m, const float* __restrict__ scores,
-                                                                       int64_t ld, int k, int32_t* __restrict__ sel,
-                                                                       int32_t* __restrict__ n_sel,
-                                                                       int32_t* __restrict__ pos,
-                                                                       int32_t* __restrict__ n_pos, int width) {
-  select_stream_row<kWritePos>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, blockIdx.x);
-}
-
 __global__ __launch_bounds__(256) void build_index_kernel(Meta m, const int32_t* __restrict__ sel,
                                                           const int32_t* __restrict__ n_sel, int k,
                                                           int32_t* __restrict__ pos, int32_t* __restrict__ n_pos,
@@ -1240,24 +708,33 @@ static void launch_select_t(const Meta& m, const float* scores, int64_t ld, int 
                                                                                    pos, n_pos, width);
     return;
   }
-  if (m.max_blocks <= kMsMinBlocks) {
-    select_reg_kernel<kMsMinBlocks / kSelectThreads, kSelectThreads, kWritePos>
+  if (m.max_blocks <= kLongRowBlocks) {
+    select_reg_kernel<kLongRowBlocks / kSelectThreads, kSelectThreads, kWritePos>
         <<<m.num_q, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
     return;
   }
-  const MsLayout l = ms_layout(m.max_blocks);
-  const dim3 grid((unsigned)m.num_q, (unsigned)l.slices);
-  ms_range_kernel<<<grid, kMsNT, 0, stream>>>(m, scores, ld, ms_ws, l);
-  ms_hist_kernel<<<grid, kMsNT, 0, stream>>>(m, scores, ld, k, ms_ws, l);
-  ms_classify_kernel<<<grid, kMsNT, 0, stream>>>(m, scores, ld, k, ms_ws, l);
-  ms_resolve_kernel<kWritePos><<<m.num_q, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos,
-                                                                         width, ms_ws, l);
-  ms_write_kernel<kWritePos><<<grid, kMsNT, 0, stream>>>(m, scores, ld, k, sel, pos, width, ms_ws, l);
+  // Longer rows: every 16,384-block slice keeps its top k, then one
+  // workgroup per query selects among the slices' candidates.
+  const int P = (m.max_blocks + kLongSlice - 1) / kLongSlice;
+  LongRows lr;
+  lr.cstride = P * k;
+  lr.cscore = reinterpret_cast<float*>(ms_ws);
+  lr.cidx = reinterpret_cast<int32_t*>(ms_ws) + (int64_t)m.num_q * lr.cstride;
+  lr.slice = 0;
+  select_slice_kernel<<<dim3((unsigned)m.num_q, (unsigned)P), kSelectThreads, 0, stream>>>(m, scores, ld, k, lr);
+  if (lr.cstride <= 16 * kSelectThreads)
+    select_cand_kernel<16, kWritePos><<<m.num_q, kSelectThreads, 0, stream>>>(m, k, sel, n_sel, pos, n_pos, width,
+                                                                               lr);
+  else
+    select_cand_kernel<32, kWritePos><<<m.num_q, kSelectThreads, 0, stream>>>(m, k, sel, n_sel, pos, n_pos, width,
+                                                                               lr);
 }
 
 size_t select_workspace_bytes(int num_q, int max_blocks) {
-  if (max_blocks <= kMsMinBlocks) return 0;
-  return (size_t)num_q * (size_t)ms_layout(max_blocks).stride * sizeof(uint32_t);
+  if (max_blocks <= kLongRowBlocks) return 0;
+  // candidate scores and block indices: slices * k of each per query (k <= 512)
+  const int64_t slices = (max_blocks + kLongSlice - 1) / kLongSlice;
+  return (size_t)num_q * (size_t)(slices * QSA_TOPK) * 2 * sizeof(uint32_t);
 }
 
 hipError_t launch_select(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel, int32_t* n_sel,
