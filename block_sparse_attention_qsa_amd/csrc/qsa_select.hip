@@ -16,7 +16,7 @@
 //     bin - falls back to exact MSB-first radix passes over order-preserving
 //     keys);
 //   * longer rows (up to 4M-token contexts): select_slice_kernel keeps the
-//     top k of every 16,384-block slice with the same body, then
+//     top k of every 8,192- or 16,384-block slice with the same body, then
 //     select_cand_kernel keeps the top k of those candidates per query.
 // Both keep every block above the threshold and the lowest-index blocks that
 // tie with it, and write sel (and, fused, pos) in ascending order.
@@ -180,14 +180,18 @@ __device__ __forceinline__ float wave_min_f32(float v) {
 // and every slice but the last keeps exactly k, so the candidate row is dense
 // and in ascending block order: the lower-index-wins rule carries over.
 constexpr int kRowQuery = 0, kRowSlice = 1, kRowCand = 2;
-constexpr int kLongSlice = 16384;            // blocks per slice of a long row
-
 struct LongRows {
   float* cscore;     // [num_q][cstride] candidate scores
   int32_t* cidx;     // [num_q][cstride] their block indices
   int cstride;       // candidate row stride: slices * k
+  int slice_blocks;  // blocks per slice
   int slice;         // kRowSlice: the slice this workgroup selects from
 };
+
+// Slices of 8,192 blocks (8 scores per thread: twice the workgroups, half
+// the work each) while the candidate rows stay within 16,384 entries, of
+// 16,384 blocks up to the longest rows (at most 64 slices, 32,768 candidates).
+inline int long_slice_blocks(int max_blocks) { return max_blocks <= 32 * 8192 ? 8192 : 16384; }
 
 // sel / pos rows for the ns kept block indices in sel_s[] (ascending),
 // nf full blocks and a partial block of pl tokens.
@@ -229,7 +233,7 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   constexpr int ER = E > 32 ? 32 : E;    // scores per thread held in registers
   constexpr int EL = E - ER;             // the rest sit in LDS, column-major
   constexpr int kMapWords = E * NT / 32;
-  static_assert(E == 16 || E == 32 || E == 64, "segment widths");
+  static_assert(E == 8 || E == 16 || E == 32 || E == 64, "segment widths");
   // candidates are staged during classification, except for 64-wide segments
   // whose register budget leaves no room for it (they stage in a loop of
   // their own)
@@ -296,8 +300,9 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   } else if (kRow == kRowSlice) {
     nf = max(0, min(S, nfq - lr.slice * S));
   } else {
-    const int P = (nfq + kLongSlice - 1) / kLongSlice;
-    nf = P <= 1 ? min(k, nfq) : (P - 1) * k + min(k, nfq - (P - 1) * kLongSlice);
+    const int SB = lr.slice_blocks;
+    const int P = (nfq + SB - 1) / SB;
+    nf = P <= 1 ? min(k, nfq) : (P - 1) * k + min(k, nfq - (P - 1) * SB);
     nf = min(nf, S);
   }
   const int pl = L & 3;
@@ -633,13 +638,13 @@ __global__ __launch_bounds__(NT) void select_reg_kernel(Meta m, const float* __r
 }
 
 // Long rows, launch 1: grid (query, slice); each workgroup keeps the top k
-// of one 16,384-block slice of its query's row.
+// of one E * 1,024-block slice of its query's row.
+template <int E>
 __global__ __launch_bounds__(kSelectThreads) void select_slice_kernel(Meta m, const float* __restrict__ scores,
                                                                       int64_t ld, int k, LongRows lr) {
   lr.slice = (int)blockIdx.y;
-  select_row<kLongSlice / kSelectThreads, kSelectThreads, false, kRowSlice>(m, scores, ld, k, nullptr, nullptr,
-                                                                             nullptr, nullptr, 0,
-                                                                             (int)blockIdx.x, lr);
+  select_row<E, kSelectThreads, false, kRowSlice>(m, scores, ld, k, nullptr, nullptr, nullptr, nullptr, 0,
+                                                  (int)blockIdx.x, lr);
 }
 
 // Long rows, launch 2: one workgroup per query keeps the top k of the
@@ -713,15 +718,19 @@ static void launch_select_t(const Meta& m, const float* scores, int64_t ld, int 
         <<<m.num_q, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
     return;
   }
-  // Longer rows: every 16,384-block slice keeps its top k, then one
-  // workgroup per query selects among the slices' candidates.
-  const int P = (m.max_blocks + kLongSlice - 1) / kLongSlice;
+  // Longer rows: every slice keeps its top k, then one workgroup per query
+  // selects among the slices' candidates.
+  const int SB = long_slice_blocks(m.max_blocks);
+  const int P = (m.max_blocks + SB - 1) / SB;
   LongRows lr;
   lr.cstride = P * k;
   lr.cscore = reinterpret_cast<float*>(ms_ws);
   lr.cidx = reinterpret_cast<int32_t*>(ms_ws) + (int64_t)m.num_q * lr.cstride;
+  lr.slice_blocks = SB;
   lr.slice = 0;
-  select_slice_kernel<<<dim3((unsigned)m.num_q, (unsigned)P), kSelectThreads, 0, stream>>>(m, scores, ld, k, lr);
+  const dim3 sgrid((unsigned)m.num_q, (unsigned)P);
+  if (SB == 8192) select_slice_kernel<8><<<sgrid, kSelectThreads, 0, stream>>>(m, scores, ld, k, lr);
+  else select_slice_kernel<16><<<sgrid, kSelectThreads, 0, stream>>>(m, scores, ld, k, lr);
   if (lr.cstride <= 16 * kSelectThreads)
     select_cand_kernel<16, kWritePos><<<m.num_q, kSelectThreads, 0, stream>>>(m, k, sel, n_sel, pos, n_pos, width,
                                                                                lr);
@@ -733,7 +742,7 @@ static void launch_select_t(const Meta& m, const float* scores, int64_t ld, int 
 size_t select_workspace_bytes(int num_q, int max_blocks) {
   if (max_blocks <= kLongRowBlocks) return 0;
   // candidate scores and block indices: slices * k of each per query (k <= 512)
-  const int64_t slices = (max_blocks + kLongSlice - 1) / kLongSlice;
+  const int64_t slices = (max_blocks + long_slice_blocks(max_blocks) - 1) / long_slice_blocks(max_blocks);
   return (size_t)num_q * (size_t)(slices * QSA_TOPK) * 2 * sizeof(uint32_t);
 }
 

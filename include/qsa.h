@@ -122,7 +122,8 @@ qsa_status qsa_score(const qsa_batch* batch, const void* idx_q, const void* ckey
  * ascending order, -1 after the last; n_sel [dev] int32 [num_q] their count.
  * scores as written by qsa_score; 1 <= k <= 512.  ws: qsa_workspace_bytes(); rows
  * longer than 32,768 blocks are selected in two steps (the top k of every
- * 16,384-block slice, then the top k of those candidates) that keep the
+ * 8,192-block slice, 16,384 past 262,144 blocks, then the top k of those
+ * candidates) that keep the
  * candidates there, shorter rows take none (ws may then be NULL). */
 qsa_status qsa_select_topk(const qsa_batch* batch, const float* scores, int64_t ld, int32_t k,
                            int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes,
