@@ -108,13 +108,17 @@ struct ElemBits {
   }
 };
 
-// Grid bin of a score: trunc(clamp((x - lo) * inv, -1, 2047)).  x - lo is
-// never negative for x >= lo, and the product, the clamp and the truncation
-// are monotone, so a larger score never lands in a lower bin and every score
-// of the row gets a bin in [0, 2047]; NaN (empty slots) gets -1.
-__device__ __forceinline__ int grid_bin(float x, float lo, float inv) {
-  float t = (x - lo) * inv;
-  t = fminf(fmaxf(t, -1.f), 2047.f);
+// Grid bin of a score, plus one: trunc(clamp(x * inv + c, 0, 2048)) with
+// c = 1.5 - lo * inv, one fused multiply-add.  The fused product, the clamp
+// and the truncation are monotone, so a larger score never lands in a lower
+// bin; NaN (empty slots) gets 0.  For x >= lo the unclamped value is 1.5 up
+// to the rounding of c, so every score of the row lands in [1, 2048] unless
+// |c| is near 2^23 (a row whose range is tiny next to its magnitude): a score
+// that then gets 0 is missed by the histogram like a NaN, and the row takes
+// the exact radix passes instead of the grid.
+__device__ __forceinline__ int grid_bin1(float x, float c, float inv) {
+  float t = __builtin_fmaf(x, inv, c);
+  t = fminf(fmaxf(t, 0.f), 2048.f);
   return (int)t;
 }
 
@@ -148,7 +152,7 @@ __device__ __forceinline__ float wave_min_f32(float v) {
 // the load to the end.
 //   1. One block reduction gives the row's smallest and largest score.  When
 //      both are finite and differ, one histogram pass bins the scores on a
-//      linear grid of 2,048 bins spanning [min, max] (grid_bin is monotone,
+//      linear grid of 2,048 bins spanning [min, max] (grid_bin1 is monotone,
 //      so the bins partition the row in score order).  On dot-product scores
 //      the grid spreads the row evenly, the histogram atomics barely collide
 //      and the bin B0 holding the k-th best score is small.
@@ -239,7 +243,11 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   // their own)
   constexpr bool kFuseStage = E <= 32;
   __shared__ float slab[EL > 0 ? EL * NT : 1];
-  __shared__ uint32_t hist[2][kRadixBins];
+  // two histograms behind one guard word: the grid pass adds at hist_g[bin + 1]
+  // and a NaN score (bin + 1 = 0) in a full wave lands in the guard, unread
+  // (the grid total then misses it and the row takes the radix passes)
+  __shared__ uint32_t hist_g[1 + 2 * kRadixBins];
+  uint32_t* const hist0 = hist_g + 1;
   __shared__ uint32_t keepmap[kMapWords];   // kept candidates, bit per block
   __shared__ float red_s[2 * NW];           // per-wave score range of the row
   __shared__ uint32_t red2_s[2 * NW];       // per-wave key range of the candidates
@@ -283,7 +291,7 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
       sv[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (beg + e) * 4, 0, 0));
   }
   // LDS set-up overlaps the loads
-  for (int i = tid; i < kRadixBins; i += NT) hist[0][i] = 0u;
+  for (int i = tid; i < kRadixBins; i += NT) hist0[i] = 0u;
   for (int i = tid; i < kMapWords; i += NT) keepmap[i] = 0u;
   if (tid == 0) s_ncand = 0u;
 
@@ -379,7 +387,9 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   const float lo = wave_min_f32(lane < NW ? red_s[NW + lane] : __builtin_inff());
   const float span = hi - lo;
   const float inv = (float)kRadixBins / span;
-  bool grid = __builtin_isfinite(lo) && __builtin_isfinite(hi) && span > 0.f && __builtin_isfinite(inv) && inv > 0.f;
+  const float cgrid = 1.5f - lo * inv;
+  bool grid = __builtin_isfinite(lo) && __builtin_isfinite(hi) && span > 0.f && __builtin_isfinite(inv) && inv > 0.f &&
+              __builtin_isfinite(cgrid);
 
   // ---- 2. grid histogram, then classification
   int B0 = 0, h = 0;
@@ -390,33 +400,33 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   constexpr bool kKeepBins = E <= 32;
   uint32_t bins[kKeepBins ? E / 2 : 1];
   if (grid) {
-    const float lo0 = fresh_uniform(lo), inv0 = fresh_uniform(inv);
+    const float c0f = fresh_uniform(cgrid), inv0 = fresh_uniform(inv);
     if (wave_full) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const int b = grid_bin(QSA_X(e), lo0, inv0);
-        atomicAdd(&hist[0][b], 1u);
+        const int b1 = grid_bin1(QSA_X(e), c0f, inv0);
+        atomicAdd(&hist_g[b1], 1u);
         if (kKeepBins) {
-          if (e & 1) bins[e >> 1] |= (uint32_t)(b + 1) << 16;
-          else bins[e >> 1] = (uint32_t)(b + 1);
+          if (e & 1) bins[e >> 1] |= (uint32_t)b1 << 16;
+          else bins[e >> 1] = (uint32_t)b1;
         }
         sched_fence(e);
       }
     } else if (!wave_empty) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const int b = grid_bin(QSA_X(e), lo0, inv0);
-        if (b >= 0) atomicAdd(&hist[0][b], 1u);
+        const int b1 = grid_bin1(QSA_X(e), c0f, inv0);
+        if (b1 > 0) atomicAdd(&hist_g[b1], 1u);
         if (kKeepBins) {
-          if (e & 1) bins[e >> 1] |= (uint32_t)(b + 1) << 16;
-          else bins[e >> 1] = (uint32_t)(b + 1);
+          if (e & 1) bins[e >> 1] |= (uint32_t)b1 << 16;
+          else bins[e >> 1] = (uint32_t)b1;
         }
         sched_fence(e);
       }
     }
-    for (int i = tid; i < kRadixBins; i += NT) hist[1][i] = 0u;
+    for (int i = tid; i < kRadixBins; i += NT) hist0[kRadixBins + i] = 0u;
     __syncthreads();
-    if (wave == 0) find_bucket(hist[0], krem, 0u, 0, &s_prefix, &s_krem, &s_count, &s_total);
+    if (wave == 0) find_bucket(hist0, krem, 0u, 0, &s_prefix, &s_krem, &s_count, &s_total);
     __syncthreads();
     h = 1;
     if (fresh_uniform(s_total) == (uint32_t)nf) {
@@ -442,12 +452,12 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
           inb.push(e, b == b1);
         }
       } else {
-        const float lo1 = fresh_uniform(lo), inv1 = fresh_uniform(inv);
+        const float c1f = fresh_uniform(cgrid), inv1 = fresh_uniform(inv);
 #pragma unroll
         for (int e = E - 1; e >= 0; --e) {
-          const int b = grid_bin(QSA_X(e), lo1, inv1);
-          above.push(e, b > B0);
-          inb.push(e, b == B0);
+          const int b1 = grid_bin1(QSA_X(e), c1f, inv1);
+          above.push(e, b1 > B0 + 1);
+          inb.push(e, b1 == B0 + 1);
           sched_fence(e);
         }
       }
@@ -545,8 +555,8 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
       for (int pass = 0; pass < 3; ++pass) {
         const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
         const uint32_t dmask = pass == 2 ? 0x3FFu : 0x7FFu;
-        uint32_t* cur = hist[h];
-        uint32_t* nxt = hist[h ^ 1];
+        uint32_t* cur = hist0 + h * kRadixBins;
+        uint32_t* nxt = hist0 + (h ^ 1) * kRadixBins;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const uint32_t key = score_key(QSA_X(e));

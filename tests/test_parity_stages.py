@@ -163,6 +163,44 @@ def test_select_small_k(k):
         assert np.array_equal(sel[i, :len(ref)], ref)
 
 
+
+@pytest.mark.parametrize("nf", [700, 12500, 20000, 70000])
+def test_select_nan_scores(nf):
+    """NaN scores (finite keys and queries never produce them) leave a valid
+    selection.  The positive quiet NaN sorts above +Inf, so a row holding a few
+    of them selects as the oracle does with +Inf in their place (no row here
+    holds an Inf).  Where a negative NaN sorts is not fixed, so that row is
+    checked for what holds either way: k distinct ascending blocks of the row
+    that include the oracle's top k - m of the row without its m NaNs.  NaNs
+    sit in full waves (grid bin -1 in the histogram pass) and the last one."""
+    need_gpu()
+    rng = np.random.default_rng(4242 + nf)
+    k = 512
+    base = rng.standard_normal((2, nf)).astype(np.float32)
+    at = np.unique(np.concatenate([[0, 5, 63, nf // 2, nf - 1], rng.choice(nf, 20, replace=False)]))
+    pos_nan = np.array([0x7FC00000], np.uint32).view(np.float32)[0]
+    neg_nan = np.array([0xFFC00000], np.uint32).view(np.float32)[0]
+    rows = base.copy()
+    rows[0, at] = pos_nan
+    rows[1, at] = neg_nan
+    say("qsa_select_topk NaN rows", nf, "NaNs", len(at))
+    b = qsa.Batch(np.arange(3), [4 * nf, 4 * nf], np.zeros(2), np.zeros(2))
+    sel = torch.full((2, k), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.full((2,), -7, dtype=torch.int32, device="cuda")
+    qsa.qsa_select_topk(b, torch.from_numpy(rows).cuda(), sel, n_sel)
+    torch.cuda.synchronize()
+    sel, n_sel = sel.cpu().numpy(), n_sel.cpu().numpy()
+    as_inf = base[0].copy()
+    as_inf[at] = np.inf
+    ref = oracle.select_blocks(as_inf, k)
+    assert n_sel[0] == k and np.array_equal(sel[0], ref)
+    got = sel[1]
+    assert n_sel[1] == k
+    assert np.all(np.diff(got) > 0) and got[0] >= 0 and got[-1] < nf
+    rest = np.delete(np.arange(nf), at)
+    top = rest[oracle.select_blocks(base[1, rest], k - len(at))]
+    assert np.all(np.isin(top, got))
+
 def test_build_index_bit_exact():
     need_gpu()
     w = _mixed_workload()
