@@ -172,7 +172,8 @@ def test_select_nan_scores(nf):
     holds an Inf).  Where a negative NaN sorts is not fixed, so that row is
     checked for what holds either way: k distinct ascending blocks of the row
     that include the oracle's top k - m of the row without its m NaNs.  NaNs
-    sit in full waves (grid bin -1 in the histogram pass) and the last one."""
+    sit in full waves (no grid bin: their histogram count goes to a guard
+    word) and in the last one."""
     need_gpu()
     rng = np.random.default_rng(4242 + nf)
     k = 512
@@ -200,6 +201,36 @@ def test_select_nan_scores(nf):
     rest = np.delete(np.arange(nf), at)
     top = rest[oracle.select_blocks(base[1, rest], k - len(at))]
     assert np.all(np.isin(top, got))
+
+
+@pytest.mark.parametrize("k", [1, 7, 100, 511])
+@pytest.mark.parametrize("kind", ["ties", "normal"])
+def test_select_small_k_long_rows(k, kind):
+    """Rows past 32,768 blocks with k < 512: every slice keeps min(k, its
+    blocks) candidates and the candidate rows are k per slice, so both slice
+    sizes (8,192 blocks up to 262,144, 16,384 beyond) and a batch mixing long,
+    short and tiny rows are checked against the oracle."""
+    need_gpu()
+    nfs = [300000, 70001, 40000, 32769, 5, 1000]
+    rows = _select_case(nfs, kind, seed=500 + k + len(kind))
+    say("qsa_select_topk long rows k", k, kind, nfs)
+    for part in (nfs, nfs[1:]):          # longest row over / under 262,144 blocks
+        off = len(nfs) - len(part)
+        b = qsa.Batch(np.arange(len(part) + 1), [4 * nf + 1 for nf in part], np.zeros(len(part)),
+                      np.zeros(len(part)))
+        S = np.zeros((len(part), b.max_blocks), np.float32)
+        for i in range(len(part)):
+            S[i, :part[i]] = rows[off + i]
+        sel = torch.full((len(part), k), -7, dtype=torch.int32, device="cuda")
+        n_sel = torch.full((len(part),), -7, dtype=torch.int32, device="cuda")
+        qsa.qsa_select_topk(b, torch.from_numpy(S).cuda(), sel, n_sel, k=k)
+        torch.cuda.synchronize()
+        sel_h, n_h = sel.cpu().numpy(), n_sel.cpu().numpy()
+        for i in range(len(part)):
+            ref = oracle.select_blocks(rows[off + i], k)
+            assert n_h[i] == len(ref), (part[i], k)
+            assert np.array_equal(sel_h[i, :len(ref)], ref), (part[i], k)
+            assert np.all(sel_h[i, len(ref):] == -1)
 
 def test_build_index_bit_exact():
     need_gpu()
