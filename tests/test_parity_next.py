@@ -128,6 +128,20 @@ def test_paged_decode(kv, page_size):
     assert np.array_equal(flat["out"].view(np.uint64), got["out"].view(np.uint64))
 
 
+
+def test_paged_decode_long_row():
+    """Paged KV with a row past 32,768 blocks (140,000 tokens): the two-step
+    long-row selection writes positions through the page table."""
+    need_gpu()
+    w = make_custom("paged-long", [140000, 57, 3001], [4, 1, 2], 16, 2, kv_dtype="fp8_e4m3", seed=712)
+    say("paged qsa_decode, long row")
+    got, table, kc, vc = _decode_paged(w, 64, 713)
+    ref = oracle.decode(w.q_start, w.seq_len, w.kv_start, w.blk_start, w.idx_q, w.ckeys, w.q, kc, vc,
+                        w.kv_dtype, w.k_scale, w.v_scale, sm_scale=SM_SCALE, want_scores=False,
+                        page_table=table, page_size=64)
+    assert_selection_equal(got, ref)
+    assert_out_close(got["out"], ref["out"])
+
 def test_draft_steps_reuse_selection():
     """A verify step selects; later draft steps of each request (after 1..4
     accepted tokens, then 0..2 more drafted ones) reuse the selection of the
