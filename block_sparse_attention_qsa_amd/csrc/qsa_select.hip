@@ -237,7 +237,7 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   constexpr int ER = E > 32 ? 32 : E;    // scores per thread held in registers
   constexpr int EL = E - ER;             // the rest sit in LDS, column-major
   constexpr int kMapWords = E * NT / 32;
-  static_assert(E == 8 || E == 16 || E == 32 || E == 64, "segment widths");
+  static_assert((E % 2 == 0 && E >= 8 && E <= 32) || E == 64, "segment widths");
   // candidates are staged during classification, except for 64-wide segments
   // whose register budget leaves no room for it (they stage in a loop of
   // their own)
@@ -268,14 +268,17 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   // [t*E, t*E + E), so the loads do not wait for the request metadata.  They
   // go through a buffer descriptor bounded by the row stride, so reads past it
   // return 0 without a branch and every load of a thread is in flight at once
-  // (slots past the query's block count are discarded afterwards).  With a
-  // stride that is a multiple of 4 a 16-byte group never straddles the bound.
+  // (slots past the query's block count are discarded afterwards).  A wide
+  // load never straddles the bound: 16-byte groups are taken when the segment
+  // width and the stride are multiples of 4, 8-byte pairs (E is even) when
+  // the stride is even, single scores otherwise.
   const int beg = tid * E;
   const uint32_t row_bytes = (uint32_t)min(max(row_ld, (int64_t)0), (int64_t)(1 << 28)) * 4u;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(srow), 0, (int)row_bytes, 0x00020000);
   float sv[E];
-  if (((kRow == kRowCand ? (int64_t)lr.cstride : ld) & 3) == 0) {
+  const int64_t rstride = kRow == kRowCand ? (int64_t)lr.cstride : ld;
+  if (E % 4 == 0 && (rstride & 3) == 0) {
 #pragma unroll
     for (int v = 0; v < E / 4; ++v) {
       const f32x4 x =
@@ -284,6 +287,14 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
       sv[4 * v + 1] = x.y;
       sv[4 * v + 2] = x.z;
       sv[4 * v + 3] = x.w;
+    }
+  } else if (E % 4 != 0 && (rstride & 1) == 0) {
+#pragma unroll
+    for (int v = 0; v < E / 2; ++v) {
+      const f32x2 x =
+          __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (beg + 2 * v) * 4, 0, 0));
+      sv[2 * v] = x.x;
+      sv[2 * v + 1] = x.y;
     }
   } else {
 #pragma unroll
@@ -521,7 +532,10 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
       keep.w[0] |= keepmap[2 * tid];
       keep.w[ElemBits<E>::W - 1] |= keepmap[2 * tid + 1];
     } else {
-      const uint32_t word = keepmap[(tid * E) >> 5] >> ((tid * E) & 31);
+      // this thread's E bits start at bit tid*E and may run into the next word
+      const int bit0 = tid * E, sh = bit0 & 31;
+      uint32_t word = keepmap[bit0 >> 5] >> sh;
+      if (sh + E > 32) word |= keepmap[(bit0 >> 5) + 1] << (32 - sh);
       keep.w[0] |= E == 32 ? word : (word & ((1u << (E & 31)) - 1u));
     }
   } else {
@@ -710,17 +724,24 @@ __global__ __launch_bounds__(256) void build_index_kernel(Meta m, const int32_t*
   if (threadIdx.x == 0) n_pos[q] = np;
 }
 
-#ifndef QSA_SELECT_NT16K
-#define QSA_SELECT_NT16K 1024
-#endif
-
 template <bool kWritePos>
 static void launch_select_t(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel, int32_t* n_sel,
                             int32_t* pos, int32_t* n_pos, int width, uint32_t* ms_ws, hipStream_t stream) {
-  constexpr int NT16 = QSA_SELECT_NT16K;                 // threads per query for rows up to 16,384 blocks
+  // Rows up to 16,384 blocks: the narrowest even segment that covers the
+  // longest row (at least 8 scores per thread), so that the busiest SIMD of
+  // the workgroup runs as few score slots as the row needs.
   if (m.max_blocks <= 16384) {
-    select_reg_kernel<16384 / NT16, NT16, kWritePos><<<m.num_q, NT16, 0, stream>>>(m, scores, ld, k, sel, n_sel,
-                                                                                   pos, n_pos, width);
+    const int e = max(8, ((m.max_blocks + kSelectThreads - 1) / kSelectThreads + 1) & ~1);
+    const dim3 g((unsigned)m.num_q);
+#define QSA_SELECT_REG(EW)                                                                               \
+  select_reg_kernel<EW, kSelectThreads, kWritePos><<<g, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, \
+                                                                                     n_sel, pos, n_pos, width)
+    if (e <= 8) QSA_SELECT_REG(8);
+    else if (e <= 10) QSA_SELECT_REG(10);
+    else if (e <= 12) QSA_SELECT_REG(12);
+    else if (e <= 14) QSA_SELECT_REG(14);
+    else QSA_SELECT_REG(16);
+#undef QSA_SELECT_REG
     return;
   }
   if (m.max_blocks <= kLongRowBlocks) {

@@ -104,6 +104,10 @@ def _select_case(nfs, kind, seed):
 SELECT_GROUPS = {
     # one launch per group: the largest row decides which selector variant runs
     "le16k": [0, 1, 511, 512, 513, 1000, 2048, 12500, 16383, 16384],
+    # the segment width follows the longest row: 10, 12 and 14 scores per thread
+    "e10": [1, 513, 9000, 10240],
+    "e12": [7, 10241, 12288],
+    "e14": [12289, 12500, 14336],
     "le32k": [3, 513, 4097, 16385, 20000, 32768],
     "le64k": [600, 32769, 40000, 65535, 65536],
     "stream": [700, 12500, 65537, 100000, 131072],
