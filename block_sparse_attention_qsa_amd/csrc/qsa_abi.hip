@@ -30,7 +30,8 @@ WsLayout ws_layout(int num_q, int max_blocks, int hq, int hkv, int k) {
   WsLayout w;
   const int width = QSA_BLOCK * k + QSA_BLOCK - 1;
   size_t off = 0;
-  w.counters = off; off += align_up((size_t)num_q * hkv * qsa::kCounterStride * sizeof(uint32_t));
+  // fixed control region first (see kCtlBytes), whatever the geometry
+  w.counters = off; off += align_up(qsa::kCtlBytes);
   w.partials = off; off += align_up(qsa::attn_partial_bytes(num_q, hkv, hq / hkv, width));
   w.attn_end = off;
   w.scores = off; off += align_up((size_t)num_q * (size_t)score_ld(max_blocks) * sizeof(float));
@@ -172,7 +173,8 @@ qsa_status qsa_sparse_attn(const qsa_batch* batch, const void* q, const void* k_
     return QSA_ERR_SHAPE;
   const int k = (width - (QSA_BLOCK - 1)) / QSA_BLOCK;
   const WsLayout w = ws_layout(batch->num_q, batch->max_blocks, num_q_heads, num_kv_heads, k);
-  QSA_TRY(check_ws(ws, ws_bytes, w.attn_end));
+  // unsplit attention (units alone fill the chip) touches no workspace
+  QSA_TRY(check_ws(ws, ws_bytes, w.attn_end > w.partials ? w.attn_end : 0));
   char* base = static_cast<char*>(ws);
   qsa::AttnArgs a;
   a.q = q;

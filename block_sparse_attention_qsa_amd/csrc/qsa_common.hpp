@@ -22,6 +22,19 @@ constexpr int kSelectThreads = 1024;   // threads of one top-k workgroup
 constexpr int kRadixBins = 2048;       // 11-bit digits: passes over bits 31..21, 20..10, 9..0
 constexpr int kMaxSplits = (QSA_WIDTH + kChunk * kAttnWaves - 1) / (kChunk * kAttnWaves);  // 17
 constexpr int kCounterStride = 32;     // uint32 words per arrival counter (one 128-byte line)
+// Attention splits a (query, KV head) unit over several workgroups only while
+// the units number fewer than this many workgroups, so at most
+// kAttnTargetWgs - 1 split-arrival counters are ever in use and their
+// indices (query * Hkv + KV head) stay below kAttnTargetWgs.
+constexpr int kAttnTargetWgs = 512;
+// Every workspace starts with a control region of fixed size that holds all
+// counters any call can use: the attention's split-arrival counters (one
+// 128-byte line per unit index) and as many lines again for the selector's
+// per-query hand-offs.  Its placement and size do not depend on the batch, so
+// one zero-filled workspace serves calls of any geometry: other calls' score
+// rows, partials or candidates never overlap a counter.
+constexpr size_t kCtlAttnBytes = (size_t)kAttnTargetWgs * kCounterStride * 4;   // 64 KiB
+constexpr size_t kCtlBytes = 2 * kCtlAttnBytes;
 // Cache-policy bit SC1 of a buffer load/store: device scope.  Such accesses
 // bypass the per-XCD caches, so workgroups on different XCDs see each
 // other's data without any cache flush or invalidation.
@@ -154,8 +167,8 @@ struct AttnSplit {
 __host__ __device__ inline AttnSplit attn_split(int num_q, int num_kv_heads, int width) {
   const int chunks = (width + kChunk - 1) / kChunk;
   const int units = num_q * num_kv_heads;
-  const int target_wgs = 512;    // two 4-wave workgroups per CU are resident at once
-  int splits = (target_wgs + units - 1) / units;
+  // two 4-wave workgroups per CU are resident at once
+  int splits = units >= kAttnTargetWgs ? 1 : (kAttnTargetWgs + units - 1) / units;
   int max_splits = (chunks + kAttnWaves - 1) / kAttnWaves;   // <= kMaxSplits for width <= QSA_WIDTH
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;

@@ -99,9 +99,15 @@ const char* qsa_status_string(int status);
 
 /* Bytes of device workspace qsa_select_topk / qsa_sparse_attn / qsa_decode need
  * for this batch and head geometry (0 when none).  The workspace must be
- * 256-byte aligned and ZERO-FILLED before its first use; every call leaves the
- * counters it uses at zero again, so one zero fill serves any number of calls
- * on the same stream.  Calls that overlap in time must not share a workspace. */
+ * 256-byte aligned and ZERO-FILLED before its first use.  It starts with a
+ * control region of fixed size (128 KiB) that holds every counter any call
+ * uses, at offsets that do not depend on the batch; the rest (scores,
+ * selections, split partials, candidates) needs no initial contents.  Every
+ * call leaves the counters it used at zero again, so one zero fill serves any
+ * number of calls, of any batch geometry, on the same stream, provided each
+ * call is given at least the bytes this function returns for its own batch
+ * (one workspace sized for the largest batch serves them all).  Calls that
+ * overlap in time must not share a workspace. */
 size_t qsa_workspace_bytes(const qsa_batch* batch, int32_t num_q_heads, int32_t num_kv_heads,
                            int32_t k);
 
@@ -149,9 +155,15 @@ qsa_status qsa_build_index(const qsa_batch* batch, const int32_t* sel, const int
  * where K(s, g) is k_cache[s][g][:] (BF16) or its FP8 E4M3FN byte decoded times
  * k_scale[g] (likewise V with v_scale).  q [dev] BF16 [num_q][Hq][128];
  * k_cache, v_cache [dev] [slots][Hkv][128] of BF16 or FP8; k_scale, v_scale [dev]
- * FP32 [Hkv], required for FP8 and ignored for BF16; pos, n_pos as from
- * qsa_build_index with width = 4k+3; out [dev] [num_q][Hq][128] FP32 (16-byte aligned) or
- * BF16 (8-byte aligned); a misaligned out is QSA_ERR_SHAPE.
+ * FP32 [Hkv], required for FP8 and ignored for BF16; out [dev] [num_q][Hq][128] FP32
+ * (16-byte aligned) or BF16 (8-byte aligned); a misaligned out is QSA_ERR_SHAPE.
+ * pos [dev] int32 [num_q][width], width = 4k+3, and n_pos [dev] int32 [num_q],
+ * 1 <= n_pos[q] <= width.  Position buffers are made of 4-slot runs, as
+ * qsa_build_index writes them (one run per kept block, then the partial
+ * block): for every i < n_pos[q],  pos[q][i] = pos[q][i - i % 4] + i % 4.
+ * The runs may come in any order; entries past n_pos[q] are not read.  A
+ * buffer that breaks the run rule gives undefined output in release builds
+ * and sets QSA_DEBUG_BAD_POSITIONS in a debug build (qsa_debug_error below).
  * Hq % Hkv == 0 and Hq / Hkv <= 16.  ws: qsa_workspace_bytes() for this k. */
 qsa_status qsa_sparse_attn(const qsa_batch* batch, const void* q, const void* k_cache,
                            const void* v_cache, int32_t kv_dtype, const float* k_scale,
@@ -175,7 +187,12 @@ qsa_status qsa_compress_keys(const qsa_batch* batch, const int32_t* prev_len, co
                              void* ckeys, hipStream_t stream);
 
 /* a1..a4 in one call, the whole decode / MTP-verify step of one QSA layer for
- * the batch: scores, selection and positions live in the workspace, and
+ * the batch.  This is the stand-in for the chain the arex-research.com article
+ * (four optimisations, item 4) overlaps with programmatic dependent launch on
+ * its hardware ("QSA logits select plus attention", 1.249 us saved at batch
+ * 1): here the stages are consecutive kernels on one stream with no host
+ * involvement between them.  Scores, selection and positions live in the
+ * workspace, and
  * sel_opt [num_q][k] / n_sel_opt / pos_opt [num_q][4k+3] / n_pos_opt, when not
  * NULL, receive copies of the selection and position buffers for inspection.
  * Arguments as for the stage calls above. */

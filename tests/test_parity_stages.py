@@ -15,6 +15,8 @@ from gpu_helpers import (SM_SCALE, assert_lean_decode_same, assert_out_close, as
 
 pytestmark = pytest.mark.gpu
 
+CTL_BYTES = 128 * 1024     # the workspace's fixed control region (all counters)
+
 
 def _mixed_workload(kv="bf16", index_values="int", hq=16, hkv=2, seed=201):
     lens = [1, 2, 3, 4, 5, 17, 300, 2051, 2055, 9000, 12345, 20000]
@@ -282,6 +284,47 @@ def test_sparse_attn_close(kv, hq, hkv, out_dtype):
             assert err.max() <= 2e-3 * np.abs(r).max()
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_sparse_attn_permuted_runs(kv):
+    """A valid position buffer whose 4-slot runs come in a shuffled order (the
+    partial block's run stays last, as the run rule requires): the output is
+    the oracle's attention over the same rows."""
+    need_gpu()
+    w = _mixed_workload(kv=kv, seed=520)
+    ref = oracle_decode(w, want_scores=False)
+    rng = np.random.default_rng(521)
+    pos = ref["pos"].copy()
+    for qi in range(w.num_q):
+        ns = (int(ref["n_pos"][qi]) // 4)            # full-block runs; the partial run stays at 4 * ns
+        runs = pos[qi, :4 * ns].reshape(ns, 4)
+        pos[qi, :4 * ns] = runs[rng.permutation(ns)].reshape(-1)
+        # the shuffled buffer still obeys pos[i] = pos[i - i % 4] + i % 4
+        i = np.arange(int(ref["n_pos"][qi]))
+        assert np.array_equal(pos[qi, i], pos[qi, i - i % 4] + i % 4)
+    assert not np.array_equal(pos, ref["pos"])
+    dev = upload(w)
+    b = batch_of(w)
+    out = torch.full((w.num_q, w.num_q_heads, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ws = qsa.alloc_workspace(b, w.num_q_heads, w.num_kv_heads)
+    say("qsa_sparse_attn permuted runs", w.name)
+    qsa.qsa_sparse_attn(b, dev["q"], dev["k_cache"], dev["v_cache"], torch.from_numpy(pos).cuda(),
+                        torch.from_numpy(ref["n_pos"]).cuda(), out, k_scale=dev["k_scale"], v_scale=dev["v_scale"],
+                        sm_scale=SM_SCALE, workspace=ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    # the oracle over the same (permuted) rows, query by query
+    for r in range(w.num_req):
+        for qi in w.queries_of(r):
+            rows = pos[qi, :int(ref["n_pos"][qi])]
+            kr = oracle.qsa_oracle._dequant(w.k_cache, rows, w.kv_dtype, w.k_scale)
+            vr = oracle.qsa_oracle._dequant(w.v_cache, rows, w.kv_dtype, w.v_scale)
+            qh = oracle.bf16_to_f64(w.q[qi])
+            exp = oracle.sparse_attention(qh, kr, vr, SM_SCALE)
+            err = np.abs(got[qi] - exp).max() / np.abs(exp).max()
+            assert err <= 2e-3, (qi, err)
+    assert_out_close(got, ref["out"])
+
+
 def test_decode_small_mixed():
     need_gpu()
     for kv in ("bf16", "fp8_e4m3"):
@@ -292,8 +335,9 @@ def test_decode_small_mixed():
         assert_selection_equal(got, ref)
         assert_out_close(got["out"], ref["out"])
         assert_lean_decode_same(w, got)
-        # split-arrival counters sit at the start of the workspace and are reset by the call
-        assert int(got["ws"][:w.num_q * w.num_kv_heads * 128].sum()) == 0
+        # every counter sits in the fixed control region at the start of the
+        # workspace (128 KiB) and the call leaves it zero again
+        assert int(got["ws"][:CTL_BYTES].sum()) == 0
 
 
 def test_decode_edge_lengths_dense_equivalence():
