@@ -19,6 +19,7 @@ import torch
 
 __all__ = ["QsaError", "Batch", "lib", "abi_version", "status_string", "workspace_bytes", "alloc_workspace",
            "qsa_score", "qsa_select_topk", "qsa_build_index", "qsa_sparse_attn", "qsa_decode", "qsa_compress_keys",
+           "qsa_decode_static", "STATIC_SCRATCH_BYTES",
            "BLOCK", "TOPK", "WIDTH", "INDEX_DIM", "HEAD_DIM", "KV_BF16", "KV_FP8_E4M3", "OUT_F32", "OUT_BF16"]
 
 BLOCK = 4
@@ -28,6 +29,7 @@ INDEX_DIM = 128
 HEAD_DIM = 128
 KV_BF16, KV_FP8_E4M3 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
+STATIC_SCRATCH_BYTES = 64 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqsa.so")
@@ -63,6 +65,8 @@ _SIGNATURES = {
     "qsa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _F, _P, _I32,
                                   _P, _P, _P, _P, _P, _SZ, _P]),
     "qsa_compress_keys": (ctypes.c_int, [_P, _P, _P, _P, _P]),
+    "qsa_decode_static": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _F, _P, _I32,
+                                         _P, _P, _P, _P, _P]),
 }
 
 
@@ -294,6 +298,31 @@ def qsa_decode(batch: Batch, idx_q, ckeys, q, k_cache, v_cache, out, workspace, 
                             _ptr(k_scale), _ptr(v_scale), hq, hkv, k, sm, _ptr(out), _out_dtype(out),
                             _ptr(sel), _ptr(n_sel), _ptr(pos), _ptr(n_pos), _ptr(workspace),
                             workspace.numel(), _stream(stream)), "qsa_decode")
+
+
+def qsa_decode_static(batch: Batch, idx_q, ckeys, q, k_cache, v_cache, out, *, k_scale=None, v_scale=None,
+                      k: int = TOPK, sm_scale: Optional[float] = None, sel=None, n_sel=None, pos=None, n_pos=None,
+                      stream=None) -> None:
+    """qsa_decode on the library's own per-device scratch (no workspace
+    argument; see qsa.h for its size limit and sharing rules)."""
+    _dev(idx_q, "idx_q", _BF16, (batch.num_q, INDEX_DIM))
+    _dev(ckeys, "ckeys", _BF16)
+    if q.dim() != 3 or q.shape[0] != batch.num_q or q.shape[2] != HEAD_DIM:
+        raise QsaError("q must be [num_q, Hq, 128]")
+    hq, hkv = int(q.shape[1]), int(k_cache.shape[1])
+    _dev(q, "q", _BF16)
+    kv = _kv_args(k_cache, v_cache, k_scale, v_scale, hkv)
+    _dev(out, "out", (torch.float32, torch.bfloat16), (batch.num_q, hq, HEAD_DIM))
+    width = BLOCK * k + BLOCK - 1
+    for name, t, shape in (("sel", sel, (batch.num_q, k)), ("n_sel", n_sel, (batch.num_q,)),
+                           ("pos", pos, (batch.num_q, width)), ("n_pos", n_pos, (batch.num_q,))):
+        if t is not None:
+            _dev(t, name, (torch.int32,), shape)
+    sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else float(sm_scale)
+    _check(lib().qsa_decode_static(batch.c, _ptr(idx_q), _ptr(ckeys), _ptr(q), _ptr(k_cache), _ptr(v_cache), kv,
+                                   _ptr(k_scale), _ptr(v_scale), hq, hkv, k, sm, _ptr(out), _out_dtype(out),
+                                   _ptr(sel), _ptr(n_sel), _ptr(pos), _ptr(n_pos), _stream(stream)),
+           "qsa_decode_static")
 
 
 def qsa_compress_keys(batch: Batch, prev_len, tok_keys, ckeys, stream=None) -> None:

@@ -3,9 +3,29 @@
 // stream; see include/qsa.h for the contract of each call.
 #include <math.h>
 
+#include <mutex>
+
 #include "qsa.h"
 #include "qsa_common.hpp"
 #include "qsa_launch.hpp"
+
+namespace qsa {
+
+// Zero-fill of n bytes (a multiple of 16) at p, as a kernel (so that it can
+// sit in a captured graph).
+__global__ __launch_bounds__(256) void zero_fill_kernel(u32x4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream) {
+  const size_t n16 = bytes / 16;
+  const unsigned grid = (unsigned)((n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024);
+  zero_fill_kernel<<<grid, 256, 0, stream>>>(static_cast<u32x4*>(p), n16);
+  return hipGetLastError();
+}
+
+}  // namespace qsa
 
 namespace {
 
@@ -107,6 +127,88 @@ inline qsa_status launched(hipError_t e) { return e == hipSuccess ? QSA_OK : QSA
     if (st_ != QSA_OK) return st_;  \
   } while (0)
 
+
+qsa_status check_decode_args(const qsa_batch* batch, const void* idx_q, const void* ckeys, const void* q,
+                             const void* k_cache, const void* v_cache, int32_t kv_dtype, const float* k_scale,
+                             const float* v_scale, int32_t num_q_heads, int32_t num_kv_heads, int32_t k,
+                             float sm_scale, void* out, int32_t out_dtype) {
+  QSA_TRY(check_batch(batch));
+  QSA_TRY(check_heads(num_q_heads, num_kv_heads));
+  QSA_TRY(check_k(k));
+  QSA_TRY(check_attn_args(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, sm_scale, out, out_dtype));
+  if (!idx_q || !ckeys) return QSA_ERR_NULL;
+  return QSA_OK;
+}
+
+// a1 -> a4 on the workspace at base (layout w, already checked).
+qsa_status decode_body(const qsa_batch* batch, const void* idx_q, const void* ckeys, const void* q,
+                       const void* k_cache, const void* v_cache, int32_t kv_dtype, const float* k_scale,
+                       const float* v_scale, int32_t num_q_heads, int32_t num_kv_heads, int32_t k, float sm_scale,
+                       void* out, int32_t out_dtype, int32_t* sel_opt, int32_t* n_sel_opt, int32_t* pos_opt,
+                       int32_t* n_pos_opt, char* base, const WsLayout& w, hipStream_t stream) {
+  const int width = QSA_BLOCK * k + QSA_BLOCK - 1;
+  float* scores = reinterpret_cast<float*>(base + w.scores);
+  int32_t* sel = sel_opt ? sel_opt : reinterpret_cast<int32_t*>(base + w.sel);
+  int32_t* n_sel = n_sel_opt ? n_sel_opt : reinterpret_cast<int32_t*>(base + w.n_sel);
+  int32_t* pos = pos_opt ? pos_opt : reinterpret_cast<int32_t*>(base + w.pos);
+  int32_t* n_pos = n_pos_opt ? n_pos_opt : reinterpret_cast<int32_t*>(base + w.n_pos);
+  const Meta m = meta_of(batch);
+  const int64_t ld = score_ld(batch->max_blocks);
+
+  QSA_TRY(launched(qsa::launch_score(m, idx_q, ckeys, scores, ld, stream)));
+  QSA_TRY(launched(qsa::launch_select(m, scores, ld, k, sel, n_sel, pos, n_pos, width, base + w.msel, stream)));
+  qsa::AttnArgs a;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.kv_fp8 = kv_dtype == QSA_KV_FP8_E4M3;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.pos = pos;
+  a.n_pos = n_pos;
+  a.width = width;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.out_bf16 = out_dtype == QSA_OUT_BF16;
+  a.partials = reinterpret_cast<float*>(base + w.partials);
+  a.counters = reinterpret_cast<uint32_t*>(base + w.counters);
+  return launched(qsa::launch_attn(m, a, stream));
+}
+
+// Scratch memory of qsa_decode_static: one copy of this array per device the
+// library runs on, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it only names the symbol): it uses the
+// device address hipGetSymbolAddress returns for the current device, looked
+// up once per device.
+__device__ __align__(256) uint8_t scratch[QSA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+char* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device address of the current device's scratch.  The first call on a
+// device looks it up and enqueues on `stream` a kernel that zero-fills its
+// control region (counters must start at zero; every later call leaves them
+// zero again).  No allocation: the array exists from the moment the library's
+// code is loaded on the device.
+qsa_status static_scratch(char** base, hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QSA_ERR_LAUNCH;
+  bool first = false;
+  std::call_once(g_scratch_once[dev], [&]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = static_cast<char*>(p);
+    first = true;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return QSA_ERR_LAUNCH;
+  if (first) QSA_TRY(launched(qsa::launch_zero_fill(g_scratch_ptr[dev], qsa::kCtlBytes, stream)));
+  *base = g_scratch_ptr[dev];
+  return QSA_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -121,6 +223,7 @@ const char* qsa_status_string(int status) {
     case QSA_ERR_UNSUPPORTED: return "unsupported dtype or head geometry";
     case QSA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case QSA_ERR_LAUNCH: return "kernel launch failed";
+    case QSA_ERR_SCRATCH: return "the batch needs more scratch than qsa_decode_static holds (QSA_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -208,43 +311,29 @@ qsa_status qsa_decode(const qsa_batch* batch, const void* idx_q, const void* cke
                       const float* v_scale, int32_t num_q_heads, int32_t num_kv_heads, int32_t k, float sm_scale,
                       void* out, int32_t out_dtype, int32_t* sel_opt, int32_t* n_sel_opt, int32_t* pos_opt,
                       int32_t* n_pos_opt, void* ws, size_t ws_bytes, hipStream_t stream) {
-  QSA_TRY(check_batch(batch));
-  QSA_TRY(check_heads(num_q_heads, num_kv_heads));
-  QSA_TRY(check_k(k));
-  QSA_TRY(check_attn_args(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, sm_scale, out, out_dtype));
-  if (!idx_q || !ckeys) return QSA_ERR_NULL;
+  QSA_TRY(check_decode_args(batch, idx_q, ckeys, q, k_cache, v_cache, kv_dtype, k_scale, v_scale, num_q_heads,
+                            num_kv_heads, k, sm_scale, out, out_dtype));
   const WsLayout w = ws_layout(batch->num_q, batch->max_blocks, num_q_heads, num_kv_heads, k);
   QSA_TRY(check_ws(ws, ws_bytes, w.total));
-  const int width = QSA_BLOCK * k + QSA_BLOCK - 1;
-  char* base = static_cast<char*>(ws);
-  float* scores = reinterpret_cast<float*>(base + w.scores);
-  int32_t* sel = sel_opt ? sel_opt : reinterpret_cast<int32_t*>(base + w.sel);
-  int32_t* n_sel = n_sel_opt ? n_sel_opt : reinterpret_cast<int32_t*>(base + w.n_sel);
-  int32_t* pos = pos_opt ? pos_opt : reinterpret_cast<int32_t*>(base + w.pos);
-  int32_t* n_pos = n_pos_opt ? n_pos_opt : reinterpret_cast<int32_t*>(base + w.n_pos);
-  const Meta m = meta_of(batch);
-  const int64_t ld = score_ld(batch->max_blocks);
+  return decode_body(batch, idx_q, ckeys, q, k_cache, v_cache, kv_dtype, k_scale, v_scale, num_q_heads,
+                     num_kv_heads, k, sm_scale, out, out_dtype, sel_opt, n_sel_opt, pos_opt, n_pos_opt,
+                     static_cast<char*>(ws), w, stream);
+}
 
-  QSA_TRY(launched(qsa::launch_score(m, idx_q, ckeys, scores, ld, stream)));
-  QSA_TRY(launched(qsa::launch_select(m, scores, ld, k, sel, n_sel, pos, n_pos, width, base + w.msel, stream)));
-  qsa::AttnArgs a;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  a.kv_fp8 = kv_dtype == QSA_KV_FP8_E4M3;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.pos = pos;
-  a.n_pos = n_pos;
-  a.width = width;
-  a.sm_scale = sm_scale;
-  a.out = out;
-  a.out_bf16 = out_dtype == QSA_OUT_BF16;
-  a.partials = reinterpret_cast<float*>(base + w.partials);
-  a.counters = reinterpret_cast<uint32_t*>(base + w.counters);
-  return launched(qsa::launch_attn(m, a, stream));
+qsa_status qsa_decode_static(const qsa_batch* batch, const void* idx_q, const void* ckeys, const void* q,
+                             const void* k_cache, const void* v_cache, int32_t kv_dtype, const float* k_scale,
+                             const float* v_scale, int32_t num_q_heads, int32_t num_kv_heads, int32_t k,
+                             float sm_scale, void* out, int32_t out_dtype, int32_t* sel_opt, int32_t* n_sel_opt,
+                             int32_t* pos_opt, int32_t* n_pos_opt, hipStream_t stream) {
+  QSA_TRY(check_decode_args(batch, idx_q, ckeys, q, k_cache, v_cache, kv_dtype, k_scale, v_scale, num_q_heads,
+                            num_kv_heads, k, sm_scale, out, out_dtype));
+  const WsLayout w = ws_layout(batch->num_q, batch->max_blocks, num_q_heads, num_kv_heads, k);
+  if (w.total > QSA_STATIC_SCRATCH_BYTES) return QSA_ERR_SCRATCH;
+  char* base = nullptr;
+  QSA_TRY(static_scratch(&base, stream));
+  return decode_body(batch, idx_q, ckeys, q, k_cache, v_cache, kv_dtype, k_scale, v_scale, num_q_heads,
+                     num_kv_heads, k, sm_scale, out, out_dtype, sel_opt, n_sel_opt, pos_opt, n_pos_opt, base, w,
+                     stream);
 }
 
 }  // extern "C"

@@ -59,6 +59,9 @@ hipError_t launch_attn(const Meta& m, const AttnArgs& a, hipStream_t stream);
 hipError_t launch_compress_keys(const Meta& m, const int32_t* prev_len, const void* tok_keys, void* ckeys,
                                 hipStream_t stream);
 
+// Zero-fills bytes (a multiple of 16) at p with a kernel on stream.
+hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
+
 // Bytes of split partials the attention needs for this geometry.
 size_t attn_partial_bytes(int num_q, int num_kv_heads, int group, int width);
 

@@ -61,6 +61,7 @@ extern "C" {
 #define QSA_MAX_GQA_GROUP 16                         /* query heads per KV head           */
 #define QSA_MAX_REQUESTS 16384                       /* num_q <= 4 * 16384 = 65536     */
 #define QSA_MAX_BLOCKS (1 << 20)                     /* full blocks per request (4M tokens) */
+#define QSA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)  /* scratch of qsa_decode_static: 64 MiB */
 
 typedef enum {
   QSA_OK = 0,
@@ -68,7 +69,9 @@ typedef enum {
   QSA_ERR_SHAPE = 2,       /* a size argument is out of range or inconsistent     */
   QSA_ERR_UNSUPPORTED = 3, /* dtype / head geometry this build does not provide   */
   QSA_ERR_WORKSPACE = 4,   /* workspace missing, misaligned or too small          */
-  QSA_ERR_LAUNCH = 5       /* the HIP runtime rejected a kernel launch            */
+  QSA_ERR_LAUNCH = 5,      /* the HIP runtime rejected a kernel launch            */
+  QSA_ERR_SCRATCH = 6      /* qsa_decode_static: the batch needs more scratch than
+                              QSA_STATIC_SCRATCH_BYTES                             */
 } qsa_status;
 
 typedef enum { QSA_KV_BF16 = 0, QSA_KV_FP8_E4M3 = 1 } qsa_kv_dtype; /* FP8 = OCP E4M3FN */
@@ -202,6 +205,28 @@ qsa_status qsa_decode(const qsa_batch* batch, const void* idx_q, const void* cke
                       int32_t num_kv_heads, int32_t k, float sm_scale, void* out,
                       int32_t out_dtype, int32_t* sel_opt, int32_t* n_sel_opt, int32_t* pos_opt,
                       int32_t* n_pos_opt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* qsa_decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  The call itself allocates nothing: its scratch
+ * (scores, selections, split partials, counters - what qsa_decode keeps in
+ * the caller's workspace) is a file-scope device array of the library,
+ * QSA_STATIC_SCRATCH_BYTES (64 MiB) per device, which every device the
+ * library runs on holds from the moment the library's code is loaded there
+ * until the process ends.  A batch whose qsa_workspace_bytes() exceeds that
+ * size is rejected with QSA_ERR_SCRATCH before anything is enqueued.  The
+ * first call on a device also enqueues, on `stream`, a kernel that zero-fills
+ * the scratch's counter region; every call leaves those counters zero again.
+ * All calls on one device share that device's scratch: calls that overlap in
+ * time on one device (other streams, other host threads) race and must be
+ * serialised by the caller.  Otherwise arguments, outputs and results are
+ * those of qsa_decode, with the same kernels. */
+qsa_status qsa_decode_static(const qsa_batch* batch, const void* idx_q, const void* ckeys, const void* q,
+                             const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                             const float* k_scale, const float* v_scale, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t k, float sm_scale, void* out,
+                             int32_t out_dtype, int32_t* sel_opt, int32_t* n_sel_opt,
+                             int32_t* pos_opt, int32_t* n_pos_opt, hipStream_t stream);
 
 #ifdef __cplusplus
 }
