@@ -59,6 +59,8 @@ WsLayout ws_layout(int num_q, int max_blocks, int hq, int hkv, int k) {
   w.n_sel = off; off += align_up((size_t)num_q * sizeof(int32_t));
   w.pos = off; off += align_up((size_t)num_q * width * sizeof(int32_t));
   w.n_pos = off; off += align_up((size_t)num_q * sizeof(int32_t));
+  // the long-row selector's slice candidates (qsa_select_topk places them
+  // right after the control region instead)
   w.msel = off; off += align_up(qsa::select_workspace_bytes(num_q, max_blocks));
   w.total = off;
   return w;
@@ -248,10 +250,13 @@ qsa_status qsa_select_topk(const qsa_batch* batch, const float* scores, int64_t 
   QSA_TRY(check_k(k));
   if (!scores || !sel || !n_sel) return QSA_ERR_NULL;
   if (ld < batch->max_blocks) return QSA_ERR_SHAPE;
-  const size_t need = qsa::select_workspace_bytes(batch->num_q, batch->max_blocks);
-  QSA_TRY(check_ws(ws, ws_bytes, need));
+  // long rows keep their slices' candidates in the workspace, after its
+  // control region (never over a counter another call may rely on)
+  const size_t cand = qsa::select_workspace_bytes(batch->num_q, batch->max_blocks);
+  QSA_TRY(check_ws(ws, ws_bytes, cand ? qsa::kCtlBytes + cand : 0));
   return launched(qsa::launch_select(meta_of(batch), scores, ld, k, sel, n_sel, nullptr, nullptr,
-                                     QSA_BLOCK * k + QSA_BLOCK - 1, ws, stream));
+                                     QSA_BLOCK * k + QSA_BLOCK - 1,
+                                     cand ? static_cast<char*>(ws) + qsa::kCtlBytes : nullptr, stream));
 }
 
 qsa_status qsa_build_index(const qsa_batch* batch, const int32_t* sel, const int32_t* n_sel, int32_t k,

@@ -227,57 +227,37 @@ __device__ __forceinline__ void write_selection(const int32_t* sel_s, int ns, in
   }
 }
 
-// The selector body for query q, run by a whole NT-thread workgroup.
-template <int E, int NT, bool kWritePos, int kRow = kRowQuery>
-__device__ __forceinline__ void select_row(const Meta& m, const float* __restrict__ scores, int64_t ld, int k,
-                                           int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
-                                           int32_t* __restrict__ pos, int32_t* __restrict__ n_pos, int width,
-                                           const int q, const LongRows& lr) {
-  constexpr int NW = NT / kWave;
-  constexpr int ER = E > 32 ? 32 : E;    // scores per thread held in registers
-  constexpr int EL = E - ER;             // the rest sit in LDS, column-major
-  constexpr int kMapWords = E * NT / 32;
-  static_assert((E % 2 == 0 && E >= 8 && E <= 32) || E == 64, "segment widths");
-  // candidates are staged during classification, except for 64-wide segments
-  // whose register budget leaves no room for it (they stage in a loop of
-  // their own)
-  constexpr bool kFuseStage = E <= 32;
-  __shared__ float slab[EL > 0 ? EL * NT : 1];
-  // two histograms behind one guard word: the grid pass adds at hist_g[bin + 1]
-  // and a NaN score (bin + 1 = 0) in a full wave lands in the guard, unread
-  // (the grid total then misses it and the row takes the radix passes)
-  __shared__ uint32_t hist_g[1 + 2 * kRadixBins];
-  uint32_t* const hist0 = hist_g + 1;
-  __shared__ uint32_t keepmap[kMapWords];   // kept candidates, bit per block
-  __shared__ float red_s[2 * NW];           // per-wave score range of the row
-  __shared__ uint32_t red2_s[2 * NW];       // per-wave key range of the candidates
-  __shared__ uint32_t scan_s[NW];
-  __shared__ u32x2 cand_s[kCandCap];
-  __shared__ int32_t sel_s[QSA_TOPK];
-  __shared__ float score_s[kRow == kRowSlice ? QSA_TOPK : 1];   // a slice's kept scores
-  __shared__ uint32_t s_prefix, s_krem, s_count, s_total, s_ncand;
+// sel / pos rows when every one of the nf <= k full blocks is kept.
+template <int NT, bool kWritePos>
+__device__ __forceinline__ void write_all_blocks(int nf, int k, int pl, const Meta& m, int r, int kv0, bool paged,
+                                                 int32_t* __restrict__ sel_row, int32_t* __restrict__ pos_row,
+                                                 int width, int32_t* __restrict__ n_sel, int32_t* __restrict__ n_pos,
+                                                 int q) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < k; i += NT) sel_row[i] = i < nf ? i : -1;
+  if (kWritePos) {
+    const int np = 4 * nf + pl;
+    for (int i = tid; i < width; i += NT) pos_row[i] = i < np ? (paged ? token_slot(m, r, i) : kv0 + i) : -1;
+  }
+  if (tid == 0) {
+    n_sel[q] = nf;
+    if (kWritePos) n_pos[q] = 4 * nf + pl;
+  }
+}
 
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  constexpr int S = E * NT;
-  const float* srow = kRow == kRowCand ? lr.cscore + (int64_t)q * lr.cstride
-                                       : scores + (int64_t)q * ld + (kRow == kRowSlice ? (int64_t)lr.slice * S : 0);
-  const int64_t row_ld = kRow == kRowCand ? (int64_t)lr.cstride
-                                          : (kRow == kRowSlice ? ld - (int64_t)lr.slice * S : ld);
-
-  // Score loads are issued first, speculatively: thread t owns the fixed segment
-  // [t*E, t*E + E), so the loads do not wait for the request metadata.  They
-  // go through a buffer descriptor bounded by the row stride, so reads past it
-  // return 0 without a branch and every load of a thread is in flight at once
-  // (slots past the query's block count are discarded afterwards).  A wide
-  // load never straddles the bound: 16-byte groups are taken when the segment
-  // width and the stride are multiples of 4, 8-byte pairs (E is even) when
-  // the stride is even, single scores otherwise.
-  const int beg = tid * E;
+// Issues the loads of thread t's segment [t*E, t*E + E) of a score row at
+// srow.  They go through a buffer descriptor bounded by row_ld floats, so
+// reads past it return 0 without a branch and every load of a thread is in
+// flight at once (slots past the row's length are discarded by the caller's
+// selection).  A wide load never straddles the bound: 16-byte groups are
+// taken when the segment width and the row stride are multiples of 4, 8-byte
+// pairs (E is even) when the stride is even, single scores otherwise.
+template <int E>
+__device__ __forceinline__ void load_segment(float (&sv)[E], const float* srow, int64_t row_ld, int64_t rstride) {
+  const int beg = threadIdx.x * E;
   const uint32_t row_bytes = (uint32_t)min(max(row_ld, (int64_t)0), (int64_t)(1 << 28)) * 4u;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(srow), 0, (int)row_bytes, 0x00020000);
-  float sv[E];
-  const int64_t rstride = kRow == kRowCand ? (int64_t)lr.cstride : ld;
   if (E % 4 == 0 && (rstride & 3) == 0) {
 #pragma unroll
     for (int v = 0; v < E / 4; ++v) {
@@ -301,70 +281,61 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
     for (int e = 0; e < E; ++e)
       sv[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (beg + e) * 4, 0, 0));
   }
-  // LDS set-up overlaps the loads
+}
+
+// The selector core, run by a whole NT-thread workgroup on one row of n
+// entries whose segment [t*E, t*E + E) thread t holds in sv (load_segment).
+// Keeps the min(k, n) entries ranked first by (score descending, slot
+// ascending) and stages their slots, ascending, in sel_s[0 .. ns) (with
+// kScores their scores in score_s); returns ns.  Ends with a barrier after
+// the staging, so sel_s can be read by any thread.
+template <int E, int NT, bool kScores>
+__device__ __forceinline__ int select_core(const float (&sv)[E], const int nf, const int k, int32_t* sel_s,
+                                           float* score_s) {
+  constexpr int NW = NT / kWave;
+  constexpr int ER = E > 32 ? 32 : E;    // scores per thread held in registers
+  constexpr int EL = E - ER;             // the rest sit in LDS, column-major
+  constexpr int kMapWords = E * NT / 32;
+  static_assert((E % 2 == 0 && E >= 8 && E <= 32) || E == 64, "segment widths");
+  // candidates are staged during classification, except for 64-wide segments
+  // whose register budget leaves no room for it (they stage in a loop of
+  // their own)
+  constexpr bool kFuseStage = E <= 32;
+  __shared__ float slab[EL > 0 ? EL * NT : 1];
+  // two histograms behind one guard word: the grid pass adds at hist_g[bin + 1]
+  // and a NaN score (bin + 1 = 0) in a full wave lands in the guard, unread
+  // (the grid total then misses it and the row takes the radix passes)
+  __shared__ uint32_t hist_g[1 + 2 * kRadixBins];
+  uint32_t* const hist0 = hist_g + 1;
+  __shared__ uint32_t keepmap[kMapWords];   // kept candidates, bit per slot
+  __shared__ float red_s[2 * NW];           // per-wave score range of the row
+  __shared__ uint32_t red2_s[2 * NW];       // per-wave key range of the candidates
+  __shared__ uint32_t scan_s[NW];
+  __shared__ u32x2 cand_s[kCandCap];
+  __shared__ uint32_t s_prefix, s_krem, s_count, s_total, s_ncand;
+
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  const int beg = tid * E;
+
+  // LDS set-up overlaps the loads still in flight
   for (int i = tid; i < kRadixBins; i += NT) hist0[i] = 0u;
   for (int i = tid; i < kMapWords; i += NT) keepmap[i] = 0u;
   if (tid == 0) s_ncand = 0u;
 
-  const int r = request_of(m.q_start, m.num_req, q);
-  const int qs = m.q_start[r];
-  const int nq = m.q_start[r + 1] - qs;
-  const int L = m.seq_len[r] - nq + 1 + (q - qs);
-  int nfq = L >> 2;                                  // the query's full blocks
-  if (nfq > m.max_blocks) nfq = m.max_blocks;
-  int nf;                                            // blocks of the row selected from here
-  if (kRow == kRowQuery) {
-    nf = min(nfq, S);                                // launcher picks E * NT >= max_blocks
-    nfq = nf;
-  } else if (kRow == kRowSlice) {
-    nf = max(0, min(S, nfq - lr.slice * S));
-  } else {
-    const int SB = lr.slice_blocks;
-    const int P = (nfq + SB - 1) / SB;
-    nf = P <= 1 ? min(k, nfq) : (P - 1) * k + min(k, nfq - (P - 1) * SB);
-    nf = min(nf, S);
-  }
-  const int pl = L & 3;
-  const bool paged = m.page_table != nullptr;
-  const int kv0 = paged ? 0 : m.kv_start[r];
-  int32_t* sel_row = kRow == kRowSlice ? nullptr : sel + (int64_t)q * k;
-  int32_t* pos_row = kWritePos ? pos + (int64_t)q * width : nullptr;
-  const int32_t* cidx_row = kRow == kRowCand ? lr.cidx + (int64_t)q * lr.cstride : nullptr;
-  float* cs_out = kRow == kRowSlice ? lr.cscore + (int64_t)q * lr.cstride + (int64_t)lr.slice * k : nullptr;
-  int32_t* ci_out = kRow == kRowSlice ? lr.cidx + (int64_t)q * lr.cstride + (int64_t)lr.slice * k : nullptr;
-
-  if (kRow == kRowSlice && nf <= k) {                // the whole slice is kept
+  const int cnt = max(0, min(E, nf - beg));
+  if (nf <= k) {
+    // every entry is kept
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (beg + e < nf) {
-        cs_out[beg + e] = sv[e];
-        ci_out[beg + e] = lr.slice * S + beg + e;
+      if (e < cnt) {
+        sel_s[beg + e] = beg + e;
+        if (kScores) score_s[beg + e] = sv[e];
       }
-    return;
-  }
-  if (kRow == kRowCand && nf <= k) {                 // every candidate is kept
-    for (int i = tid; i < nf; i += NT) sel_s[i] = cidx_row[i];
     __syncthreads();
-    write_selection<NT, kWritePos>(sel_s, nf, k, nfq, pl, m, r, kv0, paged, sel_row, pos_row, width, n_sel, n_pos,
-                                   q);
-    return;
+    return max(nf, 0);
   }
-  if (nf <= k) {
-    for (int i = tid; i < k; i += NT) sel_row[i] = i < nf ? i : -1;
-    if (kWritePos) {
-      const int np = 4 * nf + pl;
-      for (int i = tid; i < width; i += NT) pos_row[i] = i < np ? (paged ? token_slot(m, r, i) : kv0 + i) : -1;
-    }
-    if (tid == 0) {
-      n_sel[q] = nf;
-      if (kWritePos) n_pos[q] = 4 * nf + pl;
-    }
-    return;
-  }
-
-  const int cnt = max(0, min(E, nf - beg));
-  const bool wave_full = __ballot(cnt != E) == 0;    // every lane holds E blocks
-  const bool wave_empty = __ballot(cnt != 0) == 0;   // no lane holds a block
+  const bool wave_full = __ballot(cnt != E) == 0;    // every lane holds E entries
+  const bool wave_empty = __ballot(cnt != 0) == 0;   // no lane holds an entry
 
   // Slots past the row become NaN: the range reduction skips them and their
   // grid bin is -1.
@@ -490,7 +461,7 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
     }
   } else {
 #pragma unroll
-    for (int e = E - 1; e >= 0; --e) inb.push(e, e < cnt);   // every block is a candidate
+    for (int e = E - 1; e >= 0; --e) inb.push(e, e < cnt);   // every entry is a candidate
   }
 
   // ---- 3. resolve the candidates
@@ -559,7 +530,7 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
     bmax = lds_slots_max(red2_s, NW);
     bmin = lds_slots_min(red2_s + NW, NW);
     if (bmax == bmin) {
-      ties = inb;         // all tie: the lowest indices are kept
+      ties = inb;         // all tie: the lowest slots are kept
       need = krem;
     } else {
       // MSB-first radix passes (11, 11, 10 key bits) over the candidates;
@@ -631,13 +602,90 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
       t &= t - 1u;
       if (o < (uint32_t)k) {
         sel_s[o] = beg + e;
-        if (kRow == kRowSlice) score_s[o] = QSA_X(e);
+        if (kScores) score_s[o] = QSA_X(e);
       }
       ++o;
     }
   }
   const int ns = (int)min((tot >> 20) + min(tot & 0xFFFFFu, need), (uint32_t)k);
   __syncthreads();
+  return ns;
+}
+#undef QSA_X
+
+// The selector body for query q, run by a whole NT-thread workgroup: loads
+// its row (see below), handles the rows that need no selection and runs
+// select_core on the rest.
+template <int E, int NT, bool kWritePos, int kRow = kRowQuery>
+__device__ __forceinline__ void select_row(const Meta& m, const float* __restrict__ scores, int64_t ld, int k,
+                                           int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
+                                           int32_t* __restrict__ pos, int32_t* __restrict__ n_pos, int width,
+                                           const int q, const LongRows& lr) {
+  __shared__ int32_t sel_s[QSA_TOPK];
+  __shared__ float score_s[kRow == kRowSlice ? QSA_TOPK : 1];   // a slice's kept scores
+  const int tid = threadIdx.x;
+  constexpr int S = E * NT;
+  const float* srow = kRow == kRowCand ? lr.cscore + (int64_t)q * lr.cstride
+                                       : scores + (int64_t)q * ld + (kRow == kRowSlice ? (int64_t)lr.slice * S : 0);
+  const int64_t row_ld = kRow == kRowCand ? (int64_t)lr.cstride
+                                          : (kRow == kRowSlice ? ld - (int64_t)lr.slice * S : ld);
+  const int64_t rstride = kRow == kRowCand ? (int64_t)lr.cstride : ld;
+
+  // Score loads are issued first, speculatively: thread t owns the fixed
+  // segment [t*E, t*E + E), so the loads do not wait for the request metadata.
+  float sv[E];
+  load_segment<E>(sv, srow, row_ld, rstride);
+
+  const int r = request_of(m.q_start, m.num_req, q);
+  const int qs = m.q_start[r];
+  const int nq = m.q_start[r + 1] - qs;
+  const int L = m.seq_len[r] - nq + 1 + (q - qs);
+  int nfq = L >> 2;                                  // the query's full blocks
+  if (nfq > m.max_blocks) nfq = m.max_blocks;
+  int nf;                                            // entries of the row selected from here
+  if (kRow == kRowQuery) {
+    nf = min(nfq, S);                                // launcher picks E * NT >= max_blocks
+    nfq = nf;
+  } else if (kRow == kRowSlice) {
+    nf = max(0, min(S, nfq - lr.slice * S));
+  } else {
+    const int SB = lr.slice_blocks;
+    const int P = (nfq + SB - 1) / SB;
+    nf = P <= 1 ? min(k, nfq) : (P - 1) * k + min(k, nfq - (P - 1) * SB);
+    nf = min(nf, S);
+  }
+  const int pl = L & 3;
+  const bool paged = m.page_table != nullptr;
+  const int kv0 = paged ? 0 : m.kv_start[r];
+  int32_t* sel_row = kRow == kRowSlice ? nullptr : sel + (int64_t)q * k;
+  int32_t* pos_row = kWritePos ? pos + (int64_t)q * width : nullptr;
+  const int32_t* cidx_row = kRow == kRowCand ? lr.cidx + (int64_t)q * lr.cstride : nullptr;
+  float* cs_out = kRow == kRowSlice ? lr.cscore + (int64_t)q * lr.cstride + (int64_t)lr.slice * k : nullptr;
+  int32_t* ci_out = kRow == kRowSlice ? lr.cidx + (int64_t)q * lr.cstride + (int64_t)lr.slice * k : nullptr;
+  const int beg = tid * E;
+
+  if (kRow == kRowSlice && nf <= k) {                // the whole slice is kept
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (beg + e < nf) {
+        cs_out[beg + e] = sv[e];
+        ci_out[beg + e] = lr.slice * S + beg + e;
+      }
+    return;
+  }
+  if (kRow == kRowCand && nf <= k) {                 // every candidate is kept
+    for (int i = tid; i < nf; i += NT) sel_s[i] = cidx_row[i];
+    __syncthreads();
+    write_selection<NT, kWritePos>(sel_s, nf, k, nfq, pl, m, r, kv0, paged, sel_row, pos_row, width, n_sel, n_pos,
+                                   q);
+    return;
+  }
+  if (nf <= k) {
+    write_all_blocks<NT, kWritePos>(nf, k, pl, m, r, kv0, paged, sel_row, pos_row, width, n_sel, n_pos, q);
+    return;
+  }
+
+  const int ns = select_core<E, NT, kRow == kRowSlice>(sv, nf, k, sel_s, score_s);
   if (kRow == kRowSlice) {
     for (int i = tid; i < ns; i += NT) {
       cs_out[i] = score_s[i];
@@ -651,7 +699,6 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   }
   write_selection<NT, kWritePos>(sel_s, ns, k, nfq, pl, m, r, kv0, paged, sel_row, pos_row, width, n_sel, n_pos, q);
 }
-#undef QSA_X
 
 template <int E, int NT, bool kWritePos>
 __global__ __launch_bounds__(NT) void select_reg_kernel(Meta m, const float* __restrict__ scores, int64_t ld,

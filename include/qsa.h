@@ -129,11 +129,12 @@ qsa_status qsa_score(const qsa_batch* batch, const void* idx_q, const void* ckey
  * descending, block index ascending) are kept - the lower index wins ties and
  * -0.0 equals +0.0.  sel [dev] int32 [num_q][k] receives the kept block indices in
  * ascending order, -1 after the last; n_sel [dev] int32 [num_q] their count.
- * scores as written by qsa_score; 1 <= k <= 512.  ws: qsa_workspace_bytes(); rows
- * longer than 32,768 blocks are selected in two steps (the top k of every
- * 8,192-block slice, 16,384 past 262,144 blocks, then the top k of those
- * candidates) that keep the
- * candidates there, shorter rows take none (ws may then be NULL). */
+ * scores as written by qsa_score; 1 <= k <= 512.  ws: qsa_workspace_bytes() for
+ * this batch (any head counts); rows longer than 32,768 blocks are selected in
+ * two steps (the top k of every 8,192-block slice, 16,384 past 262,144 blocks,
+ * then the top k of those candidates) that keep the candidates in the
+ * workspace after its control region, so no counter is disturbed; batches of
+ * shorter rows use no workspace (ws may then be NULL). */
 qsa_status qsa_select_topk(const qsa_batch* batch, const float* scores, int64_t ld, int32_t k,
                            int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes,
                            hipStream_t stream);

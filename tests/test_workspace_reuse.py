@@ -77,3 +77,37 @@ def test_sparse_attn_one_workspace_across_geometries():
         torch.cuda.synchronize()
         assert_out_close(out.cpu().numpy().astype(np.float64), ref["out"])
         assert int(ws[:CTL_BYTES].sum().item()) == 0
+
+
+def test_long_row_select_between_decodes_on_one_workspace():
+    """The stage selector keeps long rows' slice candidates in the workspace
+    after its control region, so a qsa_select_topk call between two decode
+    calls on the same workspace disturbs no counter the decode relies on."""
+    import oracle
+    need_gpu()
+    w = make_workload("mtp50k")
+    b = batch_of(w)
+    nfs = [140001, 90000, 70001, 33000]
+    rng = np.random.default_rng(1201)
+    rows = [rng.integers(-300, 300, n).astype(np.float32) for n in nfs]
+    lb = qsa.Batch([0, 1, 2, 3, 4], [4 * n for n in nfs], [0, 0, 0, 0], [0, 0, 0, 0])
+    S = torch.zeros((4, max(nfs)), dtype=torch.float32, device="cuda")
+    for i, r in enumerate(rows):
+        S[i, :len(r)] = torch.from_numpy(r).cuda()
+    ws = torch.zeros(max(qsa.workspace_bytes(b, w.num_q_heads, w.num_kv_heads), qsa.workspace_bytes(lb, 1, 1)),
+                     dtype=torch.uint8, device="cuda")
+    ref = oracle_decode(w, want_scores=False)
+    dev = upload(w)
+    for rep in range(2):
+        got = run_decode(w, dev, ws=ws)
+        assert_selection_equal(got, ref)
+        assert_out_close(got["out"], ref["out"])
+        sel = torch.full((4, qsa.TOPK), -7, dtype=torch.int32, device="cuda")
+        n_sel = torch.full((4,), -7, dtype=torch.int32, device="cuda")
+        say("qsa_select_topk long rows on the shared workspace", rep)
+        qsa.qsa_select_topk(lb, S, sel, n_sel, workspace=ws)
+        torch.cuda.synchronize()
+        for i, r in enumerate(rows):
+            exp = oracle.select_blocks(r.astype(np.float64), qsa.TOPK)
+            assert np.array_equal(sel[i].cpu().numpy()[:len(exp)], exp), i
+        assert int(ws[:CTL_BYTES].sum().item()) == 0
