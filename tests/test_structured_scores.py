@@ -1,11 +1,9 @@
-"""The fused decode path ranks only each 64-block group's best candidates; when
-a group has all of its candidates kept (the row's best blocks crowd into few
-groups) a second pass brings in the rest of such groups.  These cases make
-that happen on purpose: index keys laid out so that whole groups win (rising
-or falling with the block index, hot groups scattered over the row, one flat
-row where every block ties), at 50,000 tokens and on a mixed batch.  The
-selection must equal the oracle's bit for bit and the output must be within
-2e-3 * max|out|."""
+"""The fused decode path on index keys laid out so that the best blocks of a
+row crowd together: scores rising or falling with the block index (whole
+64-block groups win), a few hot groups scattered over the row, and one flat
+row where every block ties (the lowest indices win).  At 50,000 tokens and on
+a mixed FP8 batch up to 131,075 tokens, the selection must equal the oracle's
+bit for bit and the output must be within 2e-3 * max|out|."""
 import numpy as np
 import pytest
 
