@@ -19,7 +19,9 @@ import torch
 
 __all__ = ["QsaError", "Batch", "lib", "abi_version", "status_string", "workspace_bytes", "alloc_workspace",
            "qsa_score", "qsa_select_topk", "qsa_build_index", "qsa_sparse_attn", "qsa_decode", "qsa_compress_keys",
-           "qsa_decode_static", "STATIC_SCRATCH_BYTES",
+           "qsa_decode_static", "STATIC_SCRATCH_BYTES", "use_library", "debug_build", "error_read",
+           "ERROR_BAD_QUERIES", "ERROR_BAD_PAGE", "ERROR_BAD_POSITIONS", "ERROR_BAD_BLOCKS",
+           "ERROR_BAD_SELECTION",
            "BLOCK", "TOPK", "WIDTH", "INDEX_DIM", "HEAD_DIM", "KV_BF16", "KV_FP8_E4M3", "OUT_F32", "OUT_BF16"]
 
 BLOCK = 4
@@ -30,59 +32,62 @@ HEAD_DIM = 128
 KV_BF16, KV_FP8_E4M3 = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 STATIC_SCRATCH_BYTES = 64 << 20
+ERROR_BAD_QUERIES, ERROR_BAD_PAGE, ERROR_BAD_POSITIONS, ERROR_BAD_BLOCKS, ERROR_BAD_SELECTION = 0x1, 0x2, 0x4, 0x8, 0x10
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqsa.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libqsa_debug.so")   # device-side precondition checks
 
 
 class QsaError(RuntimeError):
     pass
 
 
-class _CBatch(ctypes.Structure):
-    _fields_ = [("num_req", ctypes.c_int32), ("num_q", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
-                ("q_start", ctypes.c_void_p), ("seq_len", ctypes.c_void_p), ("kv_start", ctypes.c_void_p),
-                ("blk_start", ctypes.c_void_p), ("page_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
-                ("pages_per_req", ctypes.c_int32)]
-
+from ._abi import CBatch as _CBatch, load as _load_abi   # noqa: E402
 
 _lib = None
-_P = ctypes.c_void_p
-_I32 = ctypes.c_int32
-_I64 = ctypes.c_int64
-_SZ = ctypes.c_size_t
-_F = ctypes.c_float
 
-_SIGNATURES = {
-    "qsa_abi_version": (ctypes.c_int, []),
-    "qsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
-    "qsa_workspace_bytes": (_SZ, [_P, _I32, _I32, _I32]),
-    "qsa_score": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P]),
-    "qsa_select_topk": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _P, _SZ, _P]),
-    "qsa_build_index": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _P]),
-    "qsa_sparse_attn": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P, _P, _I32, _F, _P, _I32,
-                                       _P, _SZ, _P]),
-    "qsa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _F, _P, _I32,
-                                  _P, _P, _P, _P, _P, _SZ, _P]),
-    "qsa_compress_keys": (ctypes.c_int, [_P, _P, _P, _P, _P]),
-    "qsa_decode_static": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _F, _P, _I32,
-                                         _P, _P, _P, _P, _P]),
-}
+
+_use_debug = os.environ.get("QSA_DEBUG_LIBRARY", "") not in ("", "0")
+_handles = {}
+
+
+def use_library(debug: bool) -> None:
+    """Route every following call to libqsa_debug.so (debug=True: the same
+    kernels with device-side precondition checks reported in the error word)
+    or to libqsa.so."""
+    global _lib, _use_debug
+    _use_debug = bool(debug)
+    _lib = None
 
 
 def lib() -> ctypes.CDLL:
-    """Load libqsa.so (built in-tree by block_sparse_attention_qsa_amd.build)."""
+    """Load libqsa.so, or libqsa_debug.so after use_library(True) (both built
+    in-tree by block_sparse_attention_qsa_amd.build)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise QsaError(f"{LIB_PATH} is not built; run `python -m block_sparse_attention_qsa_amd.build`")
-        handle = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in _SIGNATURES.items():
-            fn = getattr(handle, name)
-            fn.restype = res
-            fn.argtypes = args
+        path = DEBUG_LIB_PATH if _use_debug else LIB_PATH
+        if path in _handles:
+            _lib = _handles[path]
+            return _lib
+        if not os.path.exists(path):
+            raise QsaError(f"{path} is not built; run `python -m block_sparse_attention_qsa_amd.build`")
+        handle = _load_abi(path)
+        _handles[path] = handle
         _lib = handle
     return _lib
+
+
+def debug_build() -> bool:
+    return bool(lib().qsa_debug_build())
+
+
+def error_read(clear: bool = False) -> int:
+    """The current device's error word (QSA_ERROR_* bits set by kernels since
+    it was last cleared); synchronises with the device."""
+    bits = ctypes.c_uint32(0)
+    _check(lib().qsa_error_read(ctypes.byref(bits), int(clear)), "qsa_error_read")
+    return int(bits.value)
 
 
 def abi_version() -> int:

@@ -106,8 +106,29 @@ qsa_status check_attn_args(const void* q, const void* kc, const void* vc, int32_
   return QSA_OK;
 }
 
+// The per-device error word (QSA_ERROR_* bits, see qsa_error_read): one copy
+// per device, zero when the library's code is loaded there.  Kernels get its
+// device address, looked up once per device.
+__device__ uint32_t error_word;
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_err_once[kMaxDevices];
+uint32_t* g_err_ptr[kMaxDevices];
+
+uint32_t* device_error_word() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_err_once[dev], [dev]() {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(error_word)) != hipSuccess) p = nullptr;
+    g_err_ptr[dev] = static_cast<uint32_t*>(p);
+  });
+  return g_err_ptr[dev];
+}
+
 Meta meta_of(const qsa_batch* b) {
   Meta m;
+  m.err = device_error_word();
   m.num_req = b->num_req;
   m.num_q = b->num_q;
   m.max_blocks = b->max_blocks;
@@ -176,6 +197,7 @@ qsa_status decode_body(const qsa_batch* batch, const void* idx_q, const void* ck
   a.out_bf16 = out_dtype == QSA_OUT_BF16;
   a.partials = reinterpret_cast<float*>(base + w.partials);
   a.counters = reinterpret_cast<uint32_t*>(base + w.counters);
+  a.err = m.err;
   return launched(qsa::launch_attn(m, a, stream));
 }
 
@@ -186,7 +208,6 @@ qsa_status decode_body(const qsa_batch* batch, const void* idx_q, const void* ck
 // up once per device.
 __device__ __align__(256) uint8_t scratch[QSA_STATIC_SCRATCH_BYTES];
 
-constexpr int kMaxDevices = 64;
 std::once_flag g_scratch_once[kMaxDevices];
 char* g_scratch_ptr[kMaxDevices];
 hipError_t g_scratch_err[kMaxDevices];
@@ -228,6 +249,26 @@ const char* qsa_status_string(int status) {
     case QSA_ERR_SCRATCH: return "the batch needs more scratch than qsa_decode_static holds (QSA_STATIC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
+}
+
+int qsa_debug_build(void) {
+#ifdef QSA_DEBUG_CHECKS
+  return 1;
+#else
+  return 0;
+#endif
+}
+
+qsa_status qsa_error_read(uint32_t* bits, int clear) {
+  if (!bits) return QSA_ERR_NULL;
+  if (hipDeviceSynchronize() != hipSuccess) return QSA_ERR_LAUNCH;
+  if (hipMemcpyFromSymbol(bits, HIP_SYMBOL(error_word), sizeof(uint32_t)) != hipSuccess) return QSA_ERR_LAUNCH;
+  if (clear) {
+    const uint32_t zero = 0u;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(error_word), &zero, sizeof(uint32_t)) != hipSuccess) return QSA_ERR_LAUNCH;
+    if (hipDeviceSynchronize() != hipSuccess) return QSA_ERR_LAUNCH;
+  }
+  return QSA_OK;
 }
 
 size_t qsa_workspace_bytes(const qsa_batch* batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t k) {
@@ -301,6 +342,7 @@ qsa_status qsa_sparse_attn(const qsa_batch* batch, const void* q, const void* k_
   a.out_bf16 = out_dtype == QSA_OUT_BF16;
   a.partials = reinterpret_cast<float*>(base + w.partials);
   a.counters = reinterpret_cast<uint32_t*>(base + w.counters);
+  a.err = device_error_word();
   return launched(qsa::launch_attn(meta_of(batch), a, stream));
 }
 

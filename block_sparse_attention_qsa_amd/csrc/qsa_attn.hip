@@ -68,6 +68,7 @@ struct AttnParams {
   void* out;
   float* part;
   uint32_t* counters;
+  uint32_t* err;            // error word (QSA_ERROR_* bits), or nullptr
   int width, num_q_heads, num_kv_heads, group;
   float sm_scale_log2;
   int splits, cps;
@@ -426,8 +427,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
     const int i = 4 * (8 * c0 + h);
     heads_s[h] = i < p.width ? prow[i] : 0;
   }
-  const int npos = p.n_pos[q];
+  const int npos_given = p.n_pos[q];
+  const int npos = min(max(npos_given, 0), p.width);   // never past the buffer
   const int slot0 = prow[0];
+#ifdef QSA_DEBUG_CHECKS
+  // the run rule over this workgroup's positions, and the length
+  if (tid == 0 && s == 0 && g == 0)
+    QSA_DCHECK(p.err, npos_given >= 1 && npos_given <= p.width, QSA_ERROR_BAD_POSITIONS);
+  for (int i = 32 * c0 + tid; i < min(32 * (c0 + p.cps), min(npos, p.width)); i += kAttnThreads)
+    QSA_DCHECK(p.err, prow[i] == prow[i & ~3] + (i & 3), QSA_ERROR_BAD_POSITIONS);
+#endif
   bf16x8 qb[4];
   {
     const uint16_t* qrow = p.q + ((int64_t)q * Hq + g * G + j) * D;
@@ -584,8 +593,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   }
   __builtin_amdgcn_s_waitcnt(0);     // this thread's stores have reached the coherence point
   __syncthreads();
+  uint32_t* const ctr = p.counters + (q * Hkv + g) * kCounterStride;
+  const int S = p.splits;
   if (tid == 0) {
-    const uint32_t ticket = atomicAdd(&p.counters[(q * Hkv + g) * kCounterStride], 1u);
+    const uint32_t ticket = atomicAdd(ctr, 1u);
     s_last = ticket == (uint32_t)(p.splits - 1);
   }
   __syncthreads();
@@ -598,7 +609,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   // outputs): lane t of the half loads split t's maximum and sum of that
   // head, the half reduces them, and each lane reads the split weights from
   // the lanes that hold them.
-  const int S = p.splits;
   const bool upper = lane >= 32;
   const int tl = lane & 31;
   static_assert(kMaxSplits <= 32, "one split per lane of a wave half");
@@ -629,7 +639,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
       store_out<kOutBf16>(p.out, ((int64_t)q * Hq + g * G) * D + 4 * v4, num);
     }
   }
-  if (tid == 0) p.counters[(q * Hkv + g) * kCounterStride] = 0u;
+  if (tid == 0) ctr[0] = 0u;
 }
 
 size_t attn_partial_bytes(int num_q, int num_kv_heads, int group, int width) {
@@ -658,6 +668,7 @@ hipError_t launch_attn(const Meta& m, const AttnArgs& a, hipStream_t stream) {
   p.sm_scale_log2 = a.sm_scale * 1.4426950408889634f;
   p.splits = sp.splits;
   p.cps = sp.chunks_per_split;
+  p.err = a.err;
   const dim3 grid((unsigned)m.num_q, (unsigned)a.num_kv_heads, (unsigned)sp.splits);
   // Large batches stream K/V with non-temporal loads (measured faster once
   // the (query, KV head) units alone fill the chip); small ones keep the

@@ -39,6 +39,7 @@ __global__ __launch_bounds__(256) void compress_keys_kernel(Meta m, const int32_
   const int lane = lane_id(), wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const int L1 = m.seq_len[r];
   int L0 = prev_len[r];
+  if (threadIdx.x == 0) QSA_DCHECK(m.err, L0 >= 0 && L0 <= L1, QSA_ERROR_BAD_QUERIES);
   L0 = L0 < 0 ? 0 : (L0 > L1 ? L1 : L0);
   const int b_end = L1 >> 2;                  // blocks with 4b + 3 < L1
   const int b_first = L0 >> 2;                // blocks with 4b + 3 >= L0

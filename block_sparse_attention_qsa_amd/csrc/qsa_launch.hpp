@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qsa.h"
+
 namespace qsa {
 
 struct Meta {
@@ -14,7 +16,22 @@ struct Meta {
   const int32_t* blk_start;
   const int32_t* page_table;   // nullptr: contiguous requests from kv_start
   int page_size, pages_per_req;
+  uint32_t* err;               // the device's error word (QSA_ERROR_* bits)
 };
+
+// Debug builds (QSA_DEBUG_CHECKS) check device-side preconditions and set a
+// bit of the error word when one fails; release builds compile the checks
+// away.  Either way the kernels go on with clamped values.
+#ifdef QSA_DEBUG_CHECKS
+#define QSA_DCHECK(err, cond, bit) \
+  do {                             \
+    if (!(cond)) atomicOr((err), (uint32_t)(bit)); \
+  } while (0)
+#else
+#define QSA_DCHECK(err, cond, bit) \
+  do {                             \
+  } while (0)
+#endif
 
 // KV slot of token t of request r: kv_start[r] + t, or through the page table
 // (page_size a multiple of 4, so a block's 4 tokens are 4 consecutive slots).
@@ -22,8 +39,11 @@ struct Meta {
 __device__ __forceinline__ int32_t token_slot(const Meta& m, int r, int t) {
   if (m.page_table == nullptr) return m.kv_start[r] + t;
   int p = t / m.page_size;
+  QSA_DCHECK(m.err, p < m.pages_per_req, QSA_ERROR_BAD_PAGE);
   p = p < m.pages_per_req ? p : m.pages_per_req - 1;
-  return m.page_table[(int64_t)r * m.pages_per_req + p] * m.page_size + t % m.page_size;
+  const int32_t page = m.page_table[(int64_t)r * m.pages_per_req + p];
+  QSA_DCHECK(m.err, page >= 0, QSA_ERROR_BAD_PAGE);
+  return page * m.page_size + t % m.page_size;
 }
 
 struct AttnArgs {
@@ -42,6 +62,7 @@ struct AttnArgs {
   int out_bf16;
   float* partials;          // split partial results (workspace)
   uint32_t* counters;       // [num_q][Hkv] split arrival counters (workspace, zero)
+  uint32_t* err;            // error word (QSA_ERROR_* bits) or nullptr
 };
 
 hipError_t launch_score(const Meta& m, const void* idx_q, const void* ckeys, float* scores, int64_t ld,

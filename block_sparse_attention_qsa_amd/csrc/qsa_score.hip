@@ -57,6 +57,10 @@ __global__ __launch_bounds__(256) void score_kernel(Meta m, const uint16_t* __re
   const int seq = m.seq_len[r], row0 = m.blk_start[r], qs = m.q_start[r], qe = m.q_start[r + 1];
   asm volatile("" ::"s"(seq), "s"(row0), "s"(qs), "s"(qe));   // keeps the four loads together, up here
   int nblk = seq >> 2;
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    QSA_DCHECK(m.err, qe - qs >= 1 && qe - qs <= QSA_MAX_Q_PER_REQ && seq >= qe - qs, QSA_ERROR_BAD_QUERIES);
+    QSA_DCHECK(m.err, nblk <= m.max_blocks, QSA_ERROR_BAD_BLOCKS);
+  }
   if (nblk > m.max_blocks) nblk = m.max_blocks;
   const int ntiles = (nblk + 15) / 16;
   const int lane = lane_id(), wave = threadIdx.x >> 6;

@@ -641,6 +641,10 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   const int nq = m.q_start[r + 1] - qs;
   const int L = m.seq_len[r] - nq + 1 + (q - qs);
   int nfq = L >> 2;                                  // the query's full blocks
+  if (tid == 0 && kRow != kRowSlice) {
+    QSA_DCHECK(m.err, nq >= 1 && nq <= QSA_MAX_Q_PER_REQ && m.seq_len[r] >= nq, QSA_ERROR_BAD_QUERIES);
+    QSA_DCHECK(m.err, nfq <= m.max_blocks, QSA_ERROR_BAD_BLOCKS);
+  }
   if (nfq > m.max_blocks) nfq = m.max_blocks;
   int nf;                                            // entries of the row selected from here
   if (kRow == kRowQuery) {
@@ -749,8 +753,15 @@ __global__ __launch_bounds__(256) void build_index_kernel(Meta m, const int32_t*
   const bool paged = m.page_table != nullptr;
   const int kv0 = paged ? 0 : m.kv_start[r];
   int given = n_sel[q];
+  QSA_DCHECK(m.err, given >= 0 && given <= k, QSA_ERROR_BAD_SELECTION);
   given = given < 0 ? 0 : (given > k ? k : given);
   const int32_t* srow = sel + (int64_t)q * k;
+#ifdef QSA_DEBUG_CHECKS
+  for (int i = threadIdx.x; i + 1 < given; i += blockDim.x)
+    QSA_DCHECK(m.err, srow[i] < srow[i + 1], QSA_ERROR_BAD_SELECTION);
+  if (threadIdx.x == 0)
+    QSA_DCHECK(m.err, nq >= 1 && nq <= QSA_MAX_Q_PER_REQ && m.seq_len[r] >= nq, QSA_ERROR_BAD_QUERIES);
+#endif
   // 256 threads, k <= 512: entries tid and tid + 256 per thread
   const int i0 = threadIdx.x, i1 = threadIdx.x + 256;
   const bool ok0 = i0 < given && srow[i0] >= 0 && srow[i0] < nf;

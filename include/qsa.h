@@ -24,9 +24,11 @@
  *   - Device-side metadata (the qsa_batch arrays) is trusted: 1 <= nq_r <= 4,
  *     nq_r <= seq_len[r], request regions inside the caches, scores finite.
  *     Kernels clamp block counts to max_blocks so that reads of the score
- *     buffer stay inside [0, ld).
+ *     buffer stay inside [0, ld), and logical pages to the page-table row.
+ *     The debug build checks these and reports breaches in the error word.
  *   - Calls on different streams with disjoint outputs and workspaces are
- *     independent; the library keeps no state between calls.
+ *     independent; the library keeps no state between calls besides the
+ *     per-device error word (qsa_error_read) and qsa_decode_static's scratch.
  *
  * Query geometry.  Request r owns queries q_start[r] .. q_start[r+1]-1 (its
  * nq_r MTP verify queries, or one decode query).  seq_len[r] counts the
@@ -74,6 +76,21 @@ typedef enum {
                               QSA_STATIC_SCRATCH_BYTES                             */
 } qsa_status;
 
+/* Bits of the per-device error word (qsa_error_read), set by the debug build
+ * (libqsa_debug.so, compiled with QSA_DEBUG_CHECKS) when a device-side
+ * metadata precondition that release builds trust does not hold.  Kernels set
+ * a bit and go on with the same clamped values release builds use; release
+ * builds never set any. */
+#define QSA_ERROR_BAD_QUERIES 0x1u    /* a request with nq_r outside 1..4, or seq_len[r] < nq_r,
+                                         or a prev_len outside 0..seq_len[r]               */
+#define QSA_ERROR_BAD_PAGE 0x2u       /* a token past the request's page-table row, or a
+                                         negative physical page                           */
+#define QSA_ERROR_BAD_POSITIONS 0x4u  /* a position buffer breaking the 4-slot run rule of
+                                         qsa_sparse_attn, or n_pos outside 1..width        */
+#define QSA_ERROR_BAD_BLOCKS 0x8u     /* seq_len[r] / 4 > max_blocks                       */
+#define QSA_ERROR_BAD_SELECTION 0x10u /* qsa_build_index given n_sel outside 0..k, or a
+                                         selection row that is not ascending              */
+
 typedef enum { QSA_KV_BF16 = 0, QSA_KV_FP8_E4M3 = 1 } qsa_kv_dtype; /* FP8 = OCP E4M3FN */
 typedef enum { QSA_OUT_F32 = 0, QSA_OUT_BF16 = 1 } qsa_out_dtype;
 
@@ -99,6 +116,16 @@ int qsa_abi_version(void);
 
 /* Static, human-readable text for a status code. */
 const char* qsa_status_string(int status);
+
+/* 1 in the debug build (device-side precondition checks), 0 otherwise. */
+int qsa_debug_build(void);
+
+/* Diagnostics: the OR of the QSA_ERROR_* bits kernels have set on the current
+ * device since the word was last cleared, into *bits [host]; clear != 0 resets
+ * it.  The word is the library's only state (one per device, zero when the
+ * library is loaded).  Unlike every other call this one synchronises: it waits
+ * for the device to finish its work and copies 4 bytes back. */
+qsa_status qsa_error_read(uint32_t* bits, int clear);
 
 /* Bytes of device workspace qsa_select_topk / qsa_sparse_attn / qsa_decode need
  * for this batch and head geometry (0 when none).  The workspace must be
