@@ -5,8 +5,15 @@ One step = one qsa_decode call = block scoring, top-k block selection, the
 position buffer and gather attention for the whole batch of one QSA layer.
 Inputs are resident in HBM before timing starts.  To measure HBM rather than
 the 256 MB last-level cache, R identical copies of every input are rotated so
-that successive calls touch at least 1 GiB of distinct bytes.  The K timed
-calls are captured in one HIP graph and bracketed by HIP events.
+that the calls of a rotation touch at least 1 GiB of distinct bytes, and when
+the K timed calls touch less than 1 GiB in all, every timed replay starts after
+1 GiB of other memory has been written.  The K timed calls are captured in one
+HIP graph and bracketed by HIP events.  The workload the metric is quoted on
+(50,000-token MTP verify at batch 1) is the headline; the batch-32 FP8
+workload, the 1M-token context and the 8K, 262K (BF16 and FP8, tied scores) and
+ragged 64-request batches are reported beside it, each with the roofline of its
+dominant kernel.  The CPU oracle on the headline workload is timed first, on
+one thread and on all host cores.
 
 Prints one JSON line (see the keys below); human-readable detail goes to stderr.
 """
@@ -109,7 +116,9 @@ class Rig:
         if name == "score":
             self.qsa.qsa_score(self.batch, c["idx_q"], c["ckeys"], self.scores)
         elif name == "select":
-            self.qsa.qsa_select_topk(self.batch, self.scores, self.sel, self.n_sel, workspace=self.sel_ws)
+            # selection and positions in one launch, the kernel qsa_decode runs
+            self.qsa.qsa_select_positions(self.batch, self.scores, self.sel, self.n_sel, self.pos, self.n_pos,
+                                          workspace=self.sel_ws)
         elif name == "attn":
             self.qsa.qsa_sparse_attn(self.batch, c["q"], c["k_cache"], c["v_cache"], self.pos, self.n_pos,
                                      self.outs[i % len(self.copies)], k_scale=c["k_scale"], v_scale=c["v_scale"],
@@ -117,9 +126,12 @@ class Rig:
         else:
             raise KeyError(name)
 
-    def timed_graph(self, fn, steps: int, warmup: int, reps: int = 3):
+    def timed_graph(self, fn, steps: int, warmup: int, reps: int = 3, flush: bool = False):
         """Capture `steps` calls of fn(i) in a HIP graph; return (median ms per
-        call over reps replays, wall-clock ms per call of the last replay)."""
+        call over reps replays, wall-clock ms per call of the last replay).
+        With flush, every timed replay is preceded (outside the timed region)
+        by writes to 1 GiB of other memory, so that calls which together touch
+        less than the last-level cache still start from HBM."""
         torch = self.torch
         for i in range(warmup):
             fn(i)
@@ -131,9 +143,12 @@ class Rig:
         torch.cuda.synchronize()
         g.replay()                      # untimed first replay
         torch.cuda.synchronize()
+        sink = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if flush else None
         times = []
         wall = None
         for _ in range(reps):
+            if flush:
+                sink.zero_()
             start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
@@ -143,7 +158,7 @@ class Rig:
             torch.cuda.synchronize()
             wall = (time.perf_counter() - t0) * 1e3 / steps
             times.append(start.elapsed_time(end) / steps)
-        del g
+        del g, sink
         return float(np.median(times)), wall
 
 
@@ -161,18 +176,23 @@ def measure(name: str, steps: int, warmup: int, kernels: bool = True) -> dict:
     nbytes = algorithmic_bytes(w)
     R = rotation_copies(w, nbytes["step"])
     rig = Rig(w, R)
-    log(f"[{name}] {R} rotating copies, {nbytes['step'] / 1e6:.2f} MB algorithmic per step")
-    ms, wall_ms = rig.timed_graph(rig.decode, steps, warmup)
+    # the timed calls rotate over the copies; when they touch less than 1 GiB
+    # in all, each timed replay starts after a cache flush
+    flush = steps * nbytes["step"] < (1 << 30)
+    log(f"[{name}] {R} rotating copies, {nbytes['step'] / 1e6:.2f} MB algorithmic per step"
+        f"{', cache flushed before each timed replay' if flush else ''}")
+    ms, wall_ms = rig.timed_graph(rig.decode, steps, warmup, flush=flush)
     gbps = nbytes["step"] / (ms * 1e-3) / 1e9
     log(f"[{name}] qsa_decode: {ms * 1e3:.2f} us/step (graph, events), wall {wall_ms * 1e3:.2f} us/step, "
         f"{gbps:.0f} GB/s = {gbps / HBM_PEAK_GBPS:.1%} of HBM peak")
-    res = {"workload": name, "w": w, "copies": R, "max_blocks": rig.batch.max_blocks,
+    res = {"workload": name, "w": w, "copies": R, "max_blocks": rig.batch.max_blocks, "flushed": flush,
            "ms_per_step": ms, "wall_ms_per_step": wall_ms,
            "steps_per_s": 1e3 / ms, "step_bytes": nbytes["step"], "step_gbps": gbps, "kernels": {}}
     if kernels:
         rig.prepare_stage_inputs()
         for st in ("score", "select", "attn"):
-            kms, _ = rig.timed_graph(lambda i, st=st: rig.stage(st, i), steps, warmup)
+            kflush = steps * nbytes[st] < (1 << 30)
+            kms, _ = rig.timed_graph(lambda i, st=st: rig.stage(st, i), steps, warmup, flush=kflush)
             kg = nbytes[st] / (kms * 1e-3) / 1e9
             res["kernels"][st] = {"us": kms * 1e3, "bytes": nbytes[st], "gbps": kg}
             log(f"[{name}]   {st:6s}: {kms * 1e3:8.2f} us/launch, {nbytes[st] / 1e6:8.3f} MB, {kg:7.0f} GB/s")
@@ -183,7 +203,7 @@ def measure(name: str, steps: int, warmup: int, kernels: bool = True) -> dict:
 
 
 KERNEL_NAMES = {"score": "qsa::score_kernel", "select": "qsa::select_reg_kernel", "attn": "qsa::attn_kernel"}
-# rows over 32,768 blocks take the five-kernel multi-workgroup top-k
+# rows over 32,768 blocks take the two-launch top-k (slices, then their candidates)
 LONG_SELECT_NAME = "qsa::select_slice_kernel + qsa::select_cand_kernel (2 launches)"
 LONG_ROW_BLOCKS = 32768
 
@@ -298,11 +318,11 @@ def stream_ceiling(gib: int = 1, reps: int = 7) -> dict:
 
 
 # ------------------------------------------------------------------ profile summaries
-PROFILE_WORKLOADS = ("mtp50k", "mtp50k_b32_fp8", "mtp1m")
+PROFILE_WORKLOADS = ("mtp50k", "mtp50k_b32_fp8", "mtp1m", "single8k", "mtp262k_ties", "mtp262k_ties_fp8", "ragged64")
 PROF_STATS_CMD = ("rocprofv3 --kernel-trace --stats -d {d}/stats_{W} -o qsa --output-format csv -- "
-                  "python -u bench.py --config {W} --b32 none --long none --steps 200 --warmup 20 --cpu-seconds 0")
+                  "python -u bench.py --config {W} --b32 none --long none --legs none --steps 200 --warmup 20 --cpu-seconds 0")
 PROF_PMC_CMD = ("rocprofv3 --pmc {C} --kernel-trace -d {d}/pmc_{C}_{W} -o qsa --output-format csv -- "
-                "python -u bench.py --config {W} --b32 none --long none --steps 10 --warmup 2 --cpu-seconds 0 "
+                "python -u bench.py --config {W} --b32 none --long none --legs none --steps 10 --warmup 2 --cpu-seconds 0 "
                 "--no-kernels --calibrate-copy")
 
 
@@ -405,26 +425,102 @@ def summarize_profiles(prof_dir: str, out_dir: str) -> None:
 
 
 # ------------------------------------------------------------------ CPU baseline
+_CPU_W = None
+
+
+def _oracle_args(w):
+    return (w.q_start, w.seq_len, w.kv_start, w.blk_start, w.idx_q, w.ckeys, w.q, w.k_cache, w.v_cache,
+            w.kv_dtype, w.k_scale, w.v_scale)
+
+
+def _cpu_worker_init(name):
+    """Each worker process of the all-cores leg: one BLAS thread, its own
+    copy of the workload."""
+    global _CPU_W
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+    from workloads import make_workload
+    _CPU_W = make_workload(name)
+
+
+def _cpu_worker_run(seconds):
+    """Full oracle steps for about `seconds`; returns (steps, elapsed)."""
+    import oracle
+    args = _oracle_args(_CPU_W)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode(*args, sm_scale=1.0 / math.sqrt(128), want_scores=False)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            return n, time.perf_counter() - t0
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(name: str, seconds: float) -> dict:
+    """The CPU oracle on full steps of the workload, median of 3 runs each:
+    on one thread, and on every host core available (one process per core,
+    one BLAS thread each, all running steps at once; steps/s is their sum).
+    Runs before the GPU is touched (the worker processes are forked)."""
+    import multiprocessing as mp
     import oracle
     from threadpoolctl import threadpool_limits
     from workloads import make_workload
     w = make_workload(name)
-    args = (w.q_start, w.seq_len, w.kv_start, w.blk_start, w.idx_q, w.ckeys, w.q, w.k_cache, w.v_cache,
-            w.kv_dtype, w.k_scale, w.v_scale)
-    n = 0
+    args = _oracle_args(w)
+    per = max(seconds / 6.0, 0.5)
+    single = []
     with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while True:
-            oracle.decode(*args, sm_scale=1.0 / math.sqrt(128), want_scores=False)
-            n += 1
-            if time.perf_counter() - t0 >= seconds:
-                break
-        dt = time.perf_counter() - t0
-    log(f"[cpu] oracle: {n} full {name} steps in {dt:.1f}s on 1 thread")
-    return {"value": round(n / dt, 4), "unit": "steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} full {name} steps ({w.num_q} queries each), single thread, "
-                      f"{os.cpu_count()} host CPUs visible"}
+        for _ in range(3):
+            n, t0 = 0, time.perf_counter()
+            while True:
+                oracle.decode(*args, sm_scale=1.0 / math.sqrt(128), want_scores=False)
+                n += 1
+                if time.perf_counter() - t0 >= per:
+                    break
+            single.append(n / (time.perf_counter() - t0))
+    cores = len(os.sched_getaffinity(0))
+    multi = []
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores, initializer=_cpu_worker_init, initargs=(name,)) as pool:
+        for _ in range(3):
+            res = pool.map(_cpu_worker_run, [per] * cores)
+            multi.append(sum(n / dt for n, dt in res))
+    v1, vn = float(np.median(single)), float(np.median(multi))
+    model = cpu_model()
+    log(f"[cpu] oracle on {name}: {v1:.2f} steps/s on 1 thread, {vn:.2f} steps/s on {cores} cores ({model})")
+    return {"value": round(vn, 4), "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"full {name} steps ({w.num_q} queries each), median of 3 runs of about {per:.1f} s: "
+                      f"{cores} processes with one BLAS thread each, steps/s summed; "
+                      f"{os.cpu_count()} CPUs in the host, {cores} available to the run",
+            "cpu_model": model,
+            "single_core": {"value": round(v1, 4), "unit": "steps/s", "cores": 1}}
+
+
+LEG_STEPS = {"mtp50k_b32_fp8": 200, "mtp1m": 100, "single8k": 1000, "mtp262k_ties": 300, "mtp262k_ties_fp8": 300,
+             "ragged64": 300}
+LEG_KEYS = {"mtp50k_b32_fp8": "b32", "mtp1m": "long"}
+
+
+def leg_line(r: dict, w, traffic) -> dict:
+    d = {"workload": r["workload"], "steps_per_s": round(r["steps_per_s"], 2),
+         "ms_per_step": round(r["ms_per_step"], 6), "step_gbps": round(r["step_gbps"], 1),
+         "step_frac_of_peak": round(r["step_gbps"] / HBM_PEAK_GBPS, 4),
+         "kernels_us": {k: round(v["us"], 3) for k, v in r["kernels"].items()},
+         "requests": w.num_req, "queries": w.num_q, "seq_len": int(w.seq_len.max()), "kv_dtype": w.kv_dtype,
+         "rotation_copies": r["copies"], "cache_flushed": r["flushed"]}
+    if r["kernels"]:
+        d["roofline"] = roofline_of(r, traffic)
+    return d
 
 
 def main():
@@ -433,11 +529,13 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="mtp50k")
-    ap.add_argument("--b32", default="mtp50k_b32_fp8", help="second workload reported beside (or 'none')")
-    ap.add_argument("--b32-steps", type=int, default=200)
+    ap.add_argument("--b32", default="mtp50k_b32_fp8", help="the batch-32 workload reported beside (or 'none')")
+    ap.add_argument("--b32-steps", type=int, default=LEG_STEPS["mtp50k_b32_fp8"])
     ap.add_argument("--long", default="mtp1m", help="long-context workload reported beside (or 'none')")
-    ap.add_argument("--long-steps", type=int, default=100)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--long-steps", type=int, default=LEG_STEPS["mtp1m"])
+    ap.add_argument("--legs", default="single8k,mtp262k_ties,mtp262k_ties_fp8,ragged64",
+                    help="further workloads reported under 'legs' (comma list, or 'none')")
+    ap.add_argument("--cpu-seconds", type=float, default=18.0)
     ap.add_argument("--no-kernels", action="store_true", help="skip the per-kernel timings")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="HBM traffic per launch measured by rocprofv3 counters")
@@ -453,6 +551,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+
+    # the CPU baseline first: its worker processes fork before the GPU is touched
+    cpu = cpu_baseline(args.config, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
     import torch
     if not torch.cuda.is_available():
@@ -476,40 +577,36 @@ def main():
         "dtype": "bf16" if w.kv_dtype == "bf16" else "bf16+fp8kv", "data": "synthetic",
         "config": {"workload": args.config, "requests": w.num_req, "queries": w.num_q,
                    "seq_len": int(w.seq_len.max()), "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
-                   "kv_dtype": w.kv_dtype, "topk": K_TOP, "rotation_copies": res["copies"]},
+                   "kv_dtype": w.kv_dtype, "topk": K_TOP, "rotation_copies": res["copies"],
+                   "cache_flushed": res["flushed"]},
         "step_gbps": round(res["step_gbps"], 1), "step_frac_of_peak": round(res["step_gbps"] / HBM_PEAK_GBPS, 4),
         "wall_ms_per_step": round(res["wall_ms_per_step"], 6),
         "kernels_us": {k: round(v["us"], 3) for k, v in res["kernels"].items()},
     }
     if res["kernels"]:
         line["roofline"] = roofline_of(res, traffic)
+    del w
+    legs = []
     if args.b32 != "none":
-        r2 = measure(args.b32, args.b32_steps, min(args.warmup, 20), kernels=not args.no_kernels)
-        w2 = r2.pop("w")
-        line["b32"] = {"workload": args.b32, "steps_per_s": round(r2["steps_per_s"], 2),
-                       "ms_per_step": round(r2["ms_per_step"], 6), "step_gbps": round(r2["step_gbps"], 1),
-                       "step_frac_of_peak": round(r2["step_gbps"] / HBM_PEAK_GBPS, 4),
-                       "kernels_us": {k: round(v["us"], 3) for k, v in r2["kernels"].items()},
-                       "requests": w2.num_req, "queries": w2.num_q, "kv_dtype": w2.kv_dtype,
-                       "rotation_copies": r2["copies"]}
-        if r2["kernels"]:
-            line["b32"]["roofline"] = roofline_of(r2, traffic)
+        legs.append((args.b32, args.b32_steps, "b32"))
     if args.long != "none":
-        r3 = measure(args.long, args.long_steps, min(args.warmup, 10), kernels=not args.no_kernels)
-        w3 = r3.pop("w")
-        line["long"] = {"workload": args.long, "steps_per_s": round(r3["steps_per_s"], 2),
-                        "ms_per_step": round(r3["ms_per_step"], 6), "step_gbps": round(r3["step_gbps"], 1),
-                        "step_frac_of_peak": round(r3["step_gbps"] / HBM_PEAK_GBPS, 4),
-                        "kernels_us": {k: round(v["us"], 3) for k, v in r3["kernels"].items()},
-                        "requests": w3.num_req, "queries": w3.num_q, "seq_len": int(w3.seq_len.max()),
-                        "kv_dtype": w3.kv_dtype, "rotation_copies": r3["copies"]}
-        if r3["kernels"]:
-            line["long"]["roofline"] = roofline_of(r3, traffic)
-        del w3
+        legs.append((args.long, args.long_steps, "long"))
+    if args.legs != "none":
+        for nm in [x for x in args.legs.split(",") if x]:
+            legs.append((nm, LEG_STEPS.get(nm, 200), None))
+    for nm, st, key in legs:
+        r = measure(nm, st, min(args.warmup, 20), kernels=not args.no_kernels)
+        wl = r.pop("w")
+        d = leg_line(r, wl, traffic)
+        if key:
+            line[key] = d
+        else:
+            line.setdefault("legs", {})[nm] = d
+        del wl
     if not args.no_kernels:
         line["stream_ceiling"] = stream_ceiling()
-    if args.cpu_seconds > 0:
-        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

@@ -19,7 +19,7 @@ import torch
 
 __all__ = ["QsaError", "Batch", "lib", "abi_version", "status_string", "workspace_bytes", "alloc_workspace",
            "qsa_score", "qsa_select_topk", "qsa_build_index", "qsa_sparse_attn", "qsa_decode", "qsa_compress_keys",
-           "qsa_decode_static", "STATIC_SCRATCH_BYTES", "use_library", "debug_build", "error_read",
+           "qsa_decode_static", "qsa_select_positions", "STATIC_SCRATCH_BYTES", "use_library", "debug_build", "error_read",
            "ERROR_BAD_QUERIES", "ERROR_BAD_PAGE", "ERROR_BAD_POSITIONS", "ERROR_BAD_BLOCKS",
            "ERROR_BAD_SELECTION",
            "BLOCK", "TOPK", "WIDTH", "INDEX_DIM", "HEAD_DIM", "KV_BF16", "KV_FP8_E4M3", "OUT_F32", "OUT_BF16"]
@@ -224,6 +224,23 @@ def qsa_select_topk(batch: Batch, scores, sel, n_sel, k: int = TOPK, workspace=N
     ws_n = workspace.numel() * workspace.element_size()
     _check(lib().qsa_select_topk(batch.c, _ptr(scores), scores.shape[1], k, _ptr(sel), _ptr(n_sel),
                                  _ptr(workspace), ws_n, _stream(stream)), "qsa_select_topk")
+
+
+def qsa_select_positions(batch: Batch, scores, sel, n_sel, pos, n_pos, k: int = TOPK, workspace=None,
+                         stream=None) -> None:
+    """Selection and position buffer in one launch (as qsa_decode runs them)."""
+    _dev(scores, "scores", (torch.float32,))
+    if scores.dim() != 2 or scores.shape[0] != batch.num_q:
+        raise QsaError("scores must be [num_q, ld]")
+    _dev(sel, "sel", (torch.int32,), (batch.num_q, k))
+    _dev(n_sel, "n_sel", (torch.int32,), (batch.num_q,))
+    _dev(pos, "pos", (torch.int32,), (batch.num_q, BLOCK * k + BLOCK - 1))
+    _dev(n_pos, "n_pos", (torch.int32,), (batch.num_q,))
+    if workspace is None:
+        workspace = alloc_workspace(batch, 1, 1, k, device=scores.device)
+    ws_n = workspace.numel() * workspace.element_size()
+    _check(lib().qsa_select_positions(batch.c, _ptr(scores), scores.shape[1], k, _ptr(sel), _ptr(n_sel), _ptr(pos),
+                                      _ptr(n_pos), _ptr(workspace), ws_n, _stream(stream)), "qsa_select_positions")
 
 
 def qsa_build_index(batch: Batch, sel, n_sel, pos, n_pos, k: int = TOPK, stream=None) -> None:

@@ -27,6 +27,7 @@ SIGNATURES = {
     "qsa_score": (ctypes.c_int, [_P, _P, _P, _P, _I64, _P]),
     "qsa_select_topk": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _P, _SZ, _P]),
     "qsa_build_index": (ctypes.c_int, [_P, _P, _P, _I32, _P, _P, _P]),
+    "qsa_select_positions": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "qsa_sparse_attn": (ctypes.c_int, [_P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _P, _P, _I32, _F, _P, _I32,
                                        _P, _SZ, _P]),
     "qsa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _P, _P, _I32, _I32, _I32, _F, _P, _I32,

@@ -300,6 +300,20 @@ qsa_status qsa_select_topk(const qsa_batch* batch, const float* scores, int64_t 
                                      cand ? static_cast<char*>(ws) + qsa::kCtlBytes : nullptr, stream));
 }
 
+qsa_status qsa_select_positions(const qsa_batch* batch, const float* scores, int64_t ld, int32_t k, int32_t* sel,
+                                int32_t* n_sel, int32_t* pos, int32_t* n_pos, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  QSA_TRY(check_batch(batch));
+  QSA_TRY(check_k(k));
+  if (!scores || !sel || !n_sel || !pos || !n_pos) return QSA_ERR_NULL;
+  if (ld < batch->max_blocks) return QSA_ERR_SHAPE;
+  const size_t cand = qsa::select_workspace_bytes(batch->num_q, batch->max_blocks);
+  QSA_TRY(check_ws(ws, ws_bytes, cand ? qsa::kCtlBytes + cand : 0));
+  return launched(qsa::launch_select(meta_of(batch), scores, ld, k, sel, n_sel, pos, n_pos,
+                                     QSA_BLOCK * k + QSA_BLOCK - 1,
+                                     cand ? static_cast<char*>(ws) + qsa::kCtlBytes : nullptr, stream));
+}
+
 qsa_status qsa_build_index(const qsa_batch* batch, const int32_t* sel, const int32_t* n_sel, int32_t k,
                            int32_t* pos, int32_t* n_pos, hipStream_t stream) {
   QSA_TRY(check_batch(batch));

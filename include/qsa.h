@@ -166,6 +166,19 @@ qsa_status qsa_select_topk(const qsa_batch* batch, const float* scores, int64_t 
                            int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* a2 + a3 in one launch, as qsa_decode runs them: the selection of
+ * qsa_select_topk and, from it, the position buffer of qsa_build_index (with
+ * the query's own full blocks, so every kept block is used), both written by
+ * the selecting kernel.  The arex-research.com article (four optimisations,
+ * item 1) keeps the selected blocks and the current partial block in one
+ * 2,051-wide buffer; the 10100.com article (first optimisation) has the
+ * selected pieces' cache positions found right after selection.  Arguments as
+ * for qsa_select_topk, plus pos [dev] int32 [num_q][4k+3] and n_pos [dev]
+ * int32 [num_q] as for qsa_build_index. */
+qsa_status qsa_select_positions(const qsa_batch* batch, const float* scores, int64_t ld, int32_t k,
+                                int32_t* sel, int32_t* n_sel, int32_t* pos, int32_t* n_pos, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
 /* a3 - position buffer.  For query q of request r, of the first min(n_sel[q], k)
  * entries of sel[q] (ascending, as qsa_select_topk writes them) the n entries
  * below nf - the blocks that are full for this query - are used:

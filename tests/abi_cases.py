@@ -84,6 +84,9 @@ def check_error_paths(lib, CBatch):
     assert lib.qsa_select_topk(ctypes.byref(long_rows), P, 40000, 512, P, P, None, 0, None) == 4   # needs workspace
     assert lib.qsa_select_topk(ctypes.byref(long_rows), P, 40000, 512, P, P, P, 1024, None) == 4
     assert lib.qsa_build_index(ctypes.byref(good), P, P, 600, P, P, None) == 2
+    assert lib.qsa_select_positions(ctypes.byref(good), P, 12500, 512, P, P, None, P, None, 0, None) == 1
+    assert lib.qsa_select_positions(ctypes.byref(good), P, 100, 512, P, P, P, P, None, 0, None) == 2
+    assert lib.qsa_select_positions(ctypes.byref(long_rows), P, 40000, 512, P, P, P, P, None, 0, None) == 4
     # attention: bad head geometry / dtype / scale / width / workspace
     args = lambda hq, hkv, kvd, ks, width, sm, odt, ws, wsn: lib.qsa_sparse_attn(
         ctypes.byref(good), P, P, P, kvd, ks, ks, hq, hkv, P, P, width, sm, P, odt, ws, wsn, None)

@@ -238,6 +238,31 @@ def test_select_small_k_long_rows(k, kind):
             assert np.array_equal(sel_h[i, :len(ref)], ref), (part[i], k)
             assert np.all(sel_h[i, len(ref):] == -1)
 
+@pytest.mark.parametrize("lens,nq", [([1, 2, 3, 4, 5, 17, 300, 2051, 2055, 9000, 12345, 20000],
+                                       [1, 2, 3, 4, 1, 4, 2, 4, 3, 4, 1, 4]),
+                                      ([140001, 33000, 5000], [4, 2, 1])])
+def test_select_positions_bit_exact(lens, nq):
+    """Selection and positions from one launch (the stage form of what
+    qsa_decode runs): both buffers bit-identical to the oracle's."""
+    need_gpu()
+    w = make_custom("selpos", lens, nq, 16, 2, seed=1401 + len(lens))
+    ref = oracle_decode(w, want_scores=False)
+    dev = upload(w)
+    b = batch_of(w)
+    scores = torch.zeros((w.num_q, b.max_blocks), dtype=torch.float32, device="cuda")
+    qsa.qsa_score(b, dev["idx_q"], dev["ckeys"], scores)
+    sel = torch.full((w.num_q, qsa.TOPK), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.full((w.num_q,), -7, dtype=torch.int32, device="cuda")
+    pos = torch.full((w.num_q, qsa.WIDTH), -7, dtype=torch.int32, device="cuda")
+    n_pos = torch.full((w.num_q,), -7, dtype=torch.int32, device="cuda")
+    say("qsa_select_positions", w.name, max(lens))
+    qsa.qsa_select_positions(b, scores, sel, n_sel, pos, n_pos)
+    torch.cuda.synchronize()
+    got = {"sel": sel.cpu().numpy(), "n_sel": n_sel.cpu().numpy(), "pos": pos.cpu().numpy(),
+           "n_pos": n_pos.cpu().numpy()}
+    assert_selection_equal(got, ref)
+
+
 def test_build_index_bit_exact():
     need_gpu()
     w = _mixed_workload()
