@@ -319,11 +319,13 @@ def stream_ceiling(gib: int = 1, reps: int = 7) -> dict:
 
 # ------------------------------------------------------------------ profile summaries
 PROFILE_WORKLOADS = ("mtp50k", "mtp50k_b32_fp8", "mtp1m", "single8k", "mtp262k_ties", "mtp262k_ties_fp8", "ragged64")
+# run from /tmp with TMPDIR=/tmp; REPO is the repository root
 PROF_STATS_CMD = ("rocprofv3 --kernel-trace --stats -d {d}/stats_{W} -o qsa --output-format csv -- "
-                  "python -u bench.py --config {W} --b32 none --long none --legs none --steps 200 --warmup 20 --cpu-seconds 0")
+                  "python -u $REPO/bench.py --config {W} --b32 none --long none --legs none --steps 200 --warmup 20 "
+                  "--cpu-seconds 0")
 PROF_PMC_CMD = ("rocprofv3 --pmc {C} --kernel-trace -d {d}/pmc_{C}_{W} -o qsa --output-format csv -- "
-                "python -u bench.py --config {W} --b32 none --long none --legs none --steps 10 --warmup 2 --cpu-seconds 0 "
-                "--no-kernels --calibrate-copy")
+                "python -u $REPO/bench.py --config {W} --b32 none --long none --legs none --steps 10 --warmup 2 "
+                "--cpu-seconds 0 --no-kernels --calibrate-copy")
 
 
 def _stage_of(kernel: str):

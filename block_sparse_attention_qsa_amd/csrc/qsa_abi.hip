@@ -178,8 +178,12 @@ qsa_status decode_body(const qsa_batch* batch, const void* idx_q, const void* ck
   const Meta m = meta_of(batch);
   const int64_t ld = score_ld(batch->max_blocks);
 
+  // Without a position buffer to return, the selector hands the attention one
+  // slot per 4-slot run (a quarter of the position rows) instead.
+  const bool run_heads = pos_opt == nullptr;
   QSA_TRY(launched(qsa::launch_score(m, idx_q, ckeys, scores, ld, stream)));
-  QSA_TRY(launched(qsa::launch_select(m, scores, ld, k, sel, n_sel, pos, n_pos, width, base + w.msel, stream)));
+  QSA_TRY(launched(qsa::launch_select(m, scores, ld, k, sel, n_sel, pos, n_pos, run_heads ? k + 1 : width, run_heads,
+                                      base + w.msel, stream)));
   qsa::AttnArgs a;
   a.q = q;
   a.k_cache = k_cache;
@@ -191,7 +195,8 @@ qsa_status decode_body(const qsa_batch* batch, const void* idx_q, const void* ck
   a.num_kv_heads = num_kv_heads;
   a.pos = pos;
   a.n_pos = n_pos;
-  a.width = width;
+  a.width = run_heads ? k + 1 : width;
+  a.run_heads = run_heads;
   a.sm_scale = sm_scale;
   a.out = out;
   a.out_bf16 = out_dtype == QSA_OUT_BF16;
@@ -296,7 +301,7 @@ qsa_status qsa_select_topk(const qsa_batch* batch, const float* scores, int64_t 
   const size_t cand = qsa::select_workspace_bytes(batch->num_q, batch->max_blocks);
   QSA_TRY(check_ws(ws, ws_bytes, cand ? qsa::kCtlBytes + cand : 0));
   return launched(qsa::launch_select(meta_of(batch), scores, ld, k, sel, n_sel, nullptr, nullptr,
-                                     QSA_BLOCK * k + QSA_BLOCK - 1,
+                                     QSA_BLOCK * k + QSA_BLOCK - 1, false,
                                      cand ? static_cast<char*>(ws) + qsa::kCtlBytes : nullptr, stream));
 }
 
@@ -310,7 +315,7 @@ qsa_status qsa_select_positions(const qsa_batch* batch, const float* scores, int
   const size_t cand = qsa::select_workspace_bytes(batch->num_q, batch->max_blocks);
   QSA_TRY(check_ws(ws, ws_bytes, cand ? qsa::kCtlBytes + cand : 0));
   return launched(qsa::launch_select(meta_of(batch), scores, ld, k, sel, n_sel, pos, n_pos,
-                                     QSA_BLOCK * k + QSA_BLOCK - 1,
+                                     QSA_BLOCK * k + QSA_BLOCK - 1, false,
                                      cand ? static_cast<char*>(ws) + qsa::kCtlBytes : nullptr, stream));
 }
 
@@ -351,6 +356,7 @@ qsa_status qsa_sparse_attn(const qsa_batch* batch, const void* q, const void* k_
   a.pos = pos;
   a.n_pos = n_pos;
   a.width = width;
+  a.run_heads = 0;
   a.sm_scale = sm_scale;
   a.out = out;
   a.out_bf16 = out_dtype == QSA_OUT_BF16;

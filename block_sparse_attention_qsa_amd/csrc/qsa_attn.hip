@@ -70,6 +70,7 @@ struct AttnParams {
   uint32_t* counters;
   uint32_t* err;            // error word (QSA_ERROR_* bits), or nullptr
   int width, num_q_heads, num_kv_heads, group;
+  int run_heads;            // pos holds one slot per 4-slot run (rows of width entries)
   float sm_scale_log2;
   int splits, cps;
 };
@@ -424,18 +425,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   // registers, with the valid length and the first slot; every load is
   // issued before any is waited for (one memory round trip).
   for (int h = tid; h < 8 * p.cps; h += kAttnThreads) {
-    const int i = 4 * (8 * c0 + h);
+    const int run = 8 * c0 + h;
+    const int i = p.run_heads ? run : 4 * run;
     heads_s[h] = i < p.width ? prow[i] : 0;
   }
   const int npos_given = p.n_pos[q];
-  const int npos = min(max(npos_given, 0), p.width);   // never past the buffer
+  // never past the buffer (a row of run heads covers 4 positions an entry)
+  const int npos = min(max(npos_given, 0), p.run_heads ? 4 * p.width : p.width);
   const int slot0 = prow[0];
 #ifdef QSA_DEBUG_CHECKS
   // the run rule over this workgroup's positions, and the length
-  if (tid == 0 && s == 0 && g == 0)
-    QSA_DCHECK(p.err, npos_given >= 1 && npos_given <= p.width, QSA_ERROR_BAD_POSITIONS);
-  for (int i = 32 * c0 + tid; i < min(32 * (c0 + p.cps), min(npos, p.width)); i += kAttnThreads)
-    QSA_DCHECK(p.err, prow[i] == prow[i & ~3] + (i & 3), QSA_ERROR_BAD_POSITIONS);
+  if (!p.run_heads) {
+    if (tid == 0 && s == 0 && g == 0)
+      QSA_DCHECK(p.err, npos_given >= 1 && npos_given <= p.width, QSA_ERROR_BAD_POSITIONS);
+    for (int i = 32 * c0 + tid; i < min(32 * (c0 + p.cps), min(npos, p.width)); i += kAttnThreads)
+      QSA_DCHECK(p.err, prow[i] == prow[i & ~3] + (i & 3), QSA_ERROR_BAD_POSITIONS);
+  }
 #endif
   bf16x8 qb[4];
   {
@@ -649,7 +654,9 @@ size_t attn_partial_bytes(int num_q, int num_kv_heads, int group, int width) {
 }
 
 hipError_t launch_attn(const Meta& m, const AttnArgs& a, hipStream_t stream) {
-  const AttnSplit sp = attn_split(m.num_q, a.num_kv_heads, a.width);
+  // the split geometry follows the positions (4 per run head)
+  const int pos_width = a.run_heads ? QSA_BLOCK * (a.width - 1) + QSA_BLOCK - 1 : a.width;
+  const AttnSplit sp = attn_split(m.num_q, a.num_kv_heads, pos_width);
   AttnParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.kc = static_cast<const uint8_t*>(a.k_cache);
@@ -662,6 +669,7 @@ hipError_t launch_attn(const Meta& m, const AttnArgs& a, hipStream_t stream) {
   p.part = a.partials;
   p.counters = a.counters;
   p.width = a.width;
+  p.run_heads = a.run_heads;
   p.num_q_heads = a.num_q_heads;
   p.num_kv_heads = a.num_kv_heads;
   p.group = a.num_q_heads / a.num_kv_heads;

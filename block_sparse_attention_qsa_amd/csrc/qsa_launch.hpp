@@ -54,9 +54,10 @@ struct AttnArgs {
   const float* v_scale;
   int kv_fp8;
   int num_q_heads, num_kv_heads;
-  const int32_t* pos;       // [num_q][width]
+  const int32_t* pos;       // [num_q][width] positions, or with run_heads one slot per 4-slot run
   const int32_t* n_pos;     // [num_q]
   int width;
+  int run_heads;
   float sm_scale;
   void* out;                // [num_q][Hq][128]
   int out_bf16;
@@ -67,12 +68,15 @@ struct AttnArgs {
 
 hipError_t launch_score(const Meta& m, const void* idx_q, const void* ckeys, float* scores, int64_t ld,
                         hipStream_t stream);
-// Writes sel/n_sel, and pos/n_pos too when pos != nullptr.  Rows longer than
-// 32,768 blocks keep their slices' candidates in select_workspace_bytes() of
-// workspace at ws (256-byte
-// aligned; no initial contents needed).
+// Writes sel/n_sel, and, when pos != nullptr, n_pos and either the position
+// rows (width entries per query) or, with run_heads, one slot per 4-slot run
+// (the first position of each kept block, then of the partial block; rows of
+// width >= k + 1 entries).  Rows longer than 32,768 blocks keep their slices'
+// candidates in select_workspace_bytes() of workspace at ws (256-byte aligned;
+// no initial contents needed).
 hipError_t launch_select(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel,
-                         int32_t* n_sel, int32_t* pos, int32_t* n_pos, int width, void* ws, hipStream_t stream);
+                         int32_t* n_sel, int32_t* pos, int32_t* n_pos, int width, bool run_heads, void* ws,
+                         hipStream_t stream);
 size_t select_workspace_bytes(int num_q, int max_blocks);
 hipError_t launch_build_index(const Meta& m, const int32_t* sel, const int32_t* n_sel, int k, int32_t* pos,
                               int32_t* n_pos, int width, hipStream_t stream);

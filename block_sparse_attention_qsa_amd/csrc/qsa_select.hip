@@ -197,9 +197,16 @@ struct LongRows {
 // 16,384 blocks up to the longest rows (at most 64 slices, 32,768 candidates).
 inline int long_slice_blocks(int max_blocks) { return max_blocks <= 32 * 8192 ? 8192 : 16384; }
 
+// What a selector writes beside sel / n_sel: nothing, the position rows
+// (width 4k + 3, -1 padded) and n_pos, or, for qsa_decode's own attention,
+// one slot per 4-slot run (the run's first position: kept blocks, then the
+// partial block; rows of k + 1 entries, those past the runs unwritten) and
+// n_pos.
+constexpr int kPosNone = 0, kPosFull = 1, kPosHeads = 2;
+
 // sel / pos rows for the ns kept block indices in sel_s[] (ascending),
 // nf full blocks and a partial block of pl tokens.
-template <int NT, bool kWritePos>
+template <int NT, int kPosOut>
 __device__ __forceinline__ void write_selection(const int32_t* sel_s, int ns, int k, int nf, int pl, const Meta& m,
                                                 int r, int kv0, bool paged, int32_t* __restrict__ sel_row,
                                                 int32_t* __restrict__ pos_row, int width,
@@ -208,7 +215,7 @@ __device__ __forceinline__ void write_selection(const int32_t* sel_s, int ns, in
   // the clamp only guards the position buffer against a broken invariant: a
   // kept index always lies in [0, nf)
   for (int i = tid; i < k; i += NT) sel_row[i] = i < ns ? min(max(sel_s[i], 0), nf - 1) : -1;
-  if (kWritePos) {
+  if (kPosOut == kPosFull) {
     const int np = 4 * ns + pl;
     for (int i = tid; i < width; i += NT) {
       int v = -1;
@@ -220,28 +227,37 @@ __device__ __forceinline__ void write_selection(const int32_t* sel_s, int ns, in
       }
       pos_row[i] = v;
     }
+  } else if (kPosOut == kPosHeads) {
+    const int nr = ns + (pl > 0 ? 1 : 0);
+    for (int i = tid; i < nr; i += NT) {
+      const int b = i < ns ? min(max(sel_s[i], 0), nf - 1) : nf;
+      pos_row[i] = paged ? token_slot(m, r, 4 * b) : kv0 + 4 * b;
+    }
   }
   if (tid == 0) {
     n_sel[q] = ns;
-    if (kWritePos) n_pos[q] = 4 * ns + pl;
+    if (kPosOut != kPosNone) n_pos[q] = 4 * ns + pl;
   }
 }
 
 // sel / pos rows when every one of the nf <= k full blocks is kept.
-template <int NT, bool kWritePos>
+template <int NT, int kPosOut>
 __device__ __forceinline__ void write_all_blocks(int nf, int k, int pl, const Meta& m, int r, int kv0, bool paged,
                                                  int32_t* __restrict__ sel_row, int32_t* __restrict__ pos_row,
                                                  int width, int32_t* __restrict__ n_sel, int32_t* __restrict__ n_pos,
                                                  int q) {
   const int tid = threadIdx.x;
   for (int i = tid; i < k; i += NT) sel_row[i] = i < nf ? i : -1;
-  if (kWritePos) {
+  if (kPosOut == kPosFull) {
     const int np = 4 * nf + pl;
     for (int i = tid; i < width; i += NT) pos_row[i] = i < np ? (paged ? token_slot(m, r, i) : kv0 + i) : -1;
+  } else if (kPosOut == kPosHeads) {
+    const int nr = nf + (pl > 0 ? 1 : 0);
+    for (int i = tid; i < nr; i += NT) pos_row[i] = paged ? token_slot(m, r, 4 * i) : kv0 + 4 * i;
   }
   if (tid == 0) {
     n_sel[q] = nf;
-    if (kWritePos) n_pos[q] = 4 * nf + pl;
+    if (kPosOut != kPosNone) n_pos[q] = 4 * nf + pl;
   }
 }
 
@@ -616,7 +632,7 @@ __device__ __forceinline__ int select_core(const float (&sv)[E], const int nf, c
 // The selector body for query q, run by a whole NT-thread workgroup: loads
 // its row (see below), handles the rows that need no selection and runs
 // select_core on the rest.
-template <int E, int NT, bool kWritePos, int kRow = kRowQuery>
+template <int E, int NT, int kPosOut, int kRow = kRowQuery>
 __device__ __forceinline__ void select_row(const Meta& m, const float* __restrict__ scores, int64_t ld, int k,
                                            int32_t* __restrict__ sel, int32_t* __restrict__ n_sel,
                                            int32_t* __restrict__ pos, int32_t* __restrict__ n_pos, int width,
@@ -662,7 +678,7 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   const bool paged = m.page_table != nullptr;
   const int kv0 = paged ? 0 : m.kv_start[r];
   int32_t* sel_row = kRow == kRowSlice ? nullptr : sel + (int64_t)q * k;
-  int32_t* pos_row = kWritePos ? pos + (int64_t)q * width : nullptr;
+  int32_t* pos_row = kPosOut != kPosNone ? pos + (int64_t)q * width : nullptr;
   const int32_t* cidx_row = kRow == kRowCand ? lr.cidx + (int64_t)q * lr.cstride : nullptr;
   float* cs_out = kRow == kRowSlice ? lr.cscore + (int64_t)q * lr.cstride + (int64_t)lr.slice * k : nullptr;
   int32_t* ci_out = kRow == kRowSlice ? lr.cidx + (int64_t)q * lr.cstride + (int64_t)lr.slice * k : nullptr;
@@ -680,12 +696,12 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   if (kRow == kRowCand && nf <= k) {                 // every candidate is kept
     for (int i = tid; i < nf; i += NT) sel_s[i] = cidx_row[i];
     __syncthreads();
-    write_selection<NT, kWritePos>(sel_s, nf, k, nfq, pl, m, r, kv0, paged, sel_row, pos_row, width, n_sel, n_pos,
+    write_selection<NT, kPosOut>(sel_s, nf, k, nfq, pl, m, r, kv0, paged, sel_row, pos_row, width, n_sel, n_pos,
                                    q);
     return;
   }
   if (nf <= k) {
-    write_all_blocks<NT, kWritePos>(nf, k, pl, m, r, kv0, paged, sel_row, pos_row, width, n_sel, n_pos, q);
+    write_all_blocks<NT, kPosOut>(nf, k, pl, m, r, kv0, paged, sel_row, pos_row, width, n_sel, n_pos, q);
     return;
   }
 
@@ -701,15 +717,15 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
     for (int i = tid; i < ns; i += NT) sel_s[i] = cidx_row[sel_s[i]];   // candidate -> block index
     __syncthreads();
   }
-  write_selection<NT, kWritePos>(sel_s, ns, k, nfq, pl, m, r, kv0, paged, sel_row, pos_row, width, n_sel, n_pos, q);
+  write_selection<NT, kPosOut>(sel_s, ns, k, nfq, pl, m, r, kv0, paged, sel_row, pos_row, width, n_sel, n_pos, q);
 }
 
-template <int E, int NT, bool kWritePos>
+template <int E, int NT, int kPosOut>
 __global__ __launch_bounds__(NT) void select_reg_kernel(Meta m, const float* __restrict__ scores, int64_t ld,
                                                         int k, int32_t* __restrict__ sel,
                                                         int32_t* __restrict__ n_sel, int32_t* __restrict__ pos,
                                                         int32_t* __restrict__ n_pos, int width) {
-  select_row<E, NT, kWritePos>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, (int)blockIdx.x, LongRows{});
+  select_row<E, NT, kPosOut>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, (int)blockIdx.x, LongRows{});
 }
 
 // Long rows, launch 1: grid (query, slice); each workgroup keeps the top k
@@ -718,19 +734,19 @@ template <int E>
 __global__ __launch_bounds__(kSelectThreads) void select_slice_kernel(Meta m, const float* __restrict__ scores,
                                                                       int64_t ld, int k, LongRows lr) {
   lr.slice = (int)blockIdx.y;
-  select_row<E, kSelectThreads, false, kRowSlice>(m, scores, ld, k, nullptr, nullptr, nullptr, nullptr, 0,
+  select_row<E, kSelectThreads, kPosNone, kRowSlice>(m, scores, ld, k, nullptr, nullptr, nullptr, nullptr, 0,
                                                   (int)blockIdx.x, lr);
 }
 
 // Long rows, launch 2: one workgroup per query keeps the top k of the
 // query's candidate row and writes sel (and pos).
-template <int E, bool kWritePos>
+template <int E, int kPosOut>
 __global__ __launch_bounds__(kSelectThreads) void select_cand_kernel(Meta m, int k, int32_t* __restrict__ sel,
                                                                      int32_t* __restrict__ n_sel,
                                                                      int32_t* __restrict__ pos,
                                                                      int32_t* __restrict__ n_pos, int width,
                                                                      LongRows lr) {
-  select_row<E, kSelectThreads, kWritePos, kRowCand>(m, nullptr, 0, k, sel, n_sel, pos, n_pos, width,
+  select_row<E, kSelectThreads, kPosOut, kRowCand>(m, nullptr, 0, k, sel, n_sel, pos, n_pos, width,
                                                       (int)blockIdx.x, lr);
 }
 
@@ -782,7 +798,7 @@ __global__ __launch_bounds__(256) void build_index_kernel(Meta m, const int32_t*
   if (threadIdx.x == 0) n_pos[q] = np;
 }
 
-template <bool kWritePos>
+template <int kPosOut>
 static void launch_select_t(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel, int32_t* n_sel,
                             int32_t* pos, int32_t* n_pos, int width, uint32_t* ms_ws, hipStream_t stream) {
   // Rows up to 16,384 blocks: the narrowest even segment that covers the
@@ -792,7 +808,7 @@ static void launch_select_t(const Meta& m, const float* scores, int64_t ld, int 
     const int e = max(8, ((m.max_blocks + kSelectThreads - 1) / kSelectThreads + 1) & ~1);
     const dim3 g((unsigned)m.num_q);
 #define QSA_SELECT_REG(EW)                                                                               \
-  select_reg_kernel<EW, kSelectThreads, kWritePos><<<g, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, \
+  select_reg_kernel<EW, kSelectThreads, kPosOut><<<g, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, \
                                                                                      n_sel, pos, n_pos, width)
     if (e <= 8) QSA_SELECT_REG(8);
     else if (e <= 10) QSA_SELECT_REG(10);
@@ -803,7 +819,7 @@ static void launch_select_t(const Meta& m, const float* scores, int64_t ld, int 
     return;
   }
   if (m.max_blocks <= kLongRowBlocks) {
-    select_reg_kernel<kLongRowBlocks / kSelectThreads, kSelectThreads, kWritePos>
+    select_reg_kernel<kLongRowBlocks / kSelectThreads, kSelectThreads, kPosOut>
         <<<m.num_q, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
     return;
   }
@@ -821,10 +837,10 @@ static void launch_select_t(const Meta& m, const float* scores, int64_t ld, int 
   if (SB == 8192) select_slice_kernel<8><<<sgrid, kSelectThreads, 0, stream>>>(m, scores, ld, k, lr);
   else select_slice_kernel<16><<<sgrid, kSelectThreads, 0, stream>>>(m, scores, ld, k, lr);
   if (lr.cstride <= 16 * kSelectThreads)
-    select_cand_kernel<16, kWritePos><<<m.num_q, kSelectThreads, 0, stream>>>(m, k, sel, n_sel, pos, n_pos, width,
+    select_cand_kernel<16, kPosOut><<<m.num_q, kSelectThreads, 0, stream>>>(m, k, sel, n_sel, pos, n_pos, width,
                                                                                lr);
   else
-    select_cand_kernel<32, kWritePos><<<m.num_q, kSelectThreads, 0, stream>>>(m, k, sel, n_sel, pos, n_pos, width,
+    select_cand_kernel<32, kPosOut><<<m.num_q, kSelectThreads, 0, stream>>>(m, k, sel, n_sel, pos, n_pos, width,
                                                                                lr);
 }
 
@@ -836,12 +852,14 @@ size_t select_workspace_bytes(int num_q, int max_blocks) {
 }
 
 hipError_t launch_select(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel, int32_t* n_sel,
-                         int32_t* pos, int32_t* n_pos, int width, void* ws, hipStream_t stream) {
+                         int32_t* pos, int32_t* n_pos, int width, bool run_heads, void* ws, hipStream_t stream) {
   uint32_t* ms_ws = static_cast<uint32_t*>(ws);
-  if (pos)
-    launch_select_t<true>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, ms_ws, stream);
+  if (pos && run_heads)
+    launch_select_t<kPosHeads>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, ms_ws, stream);
+  else if (pos)
+    launch_select_t<kPosFull>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, ms_ws, stream);
   else
-    launch_select_t<false>(m, scores, ld, k, sel, n_sel, nullptr, nullptr, width, ms_ws, stream);
+    launch_select_t<kPosNone>(m, scores, ld, k, sel, n_sel, nullptr, nullptr, width, ms_ws, stream);
   return hipGetLastError();
 }
 
