@@ -53,7 +53,11 @@ __device__ __forceinline__ float load_coherent_f32(__amdgpu_buffer_rsrc_t r, int
 __device__ __forceinline__ void store_coherent_f32(__amdgpu_buffer_rsrc_t r, int float_off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, float_off * 4, 0, kCpolDevice);
 }
-constexpr int kMaxHeads = 8 * ((QSA_WIDTH + kChunk - 1) / kChunk);   // block heads of one split
+// Block heads of one split: 8 per chunk, for the most chunks a split takes
+// (a whole 2,051-position row, its 65 chunks rounded up to whole 4-chunk
+// steps).
+constexpr int kMaxSplitChunks = ((QSA_WIDTH + kChunk - 1) / kChunk + kAttnWaves - 1) / kAttnWaves * kAttnWaves;
+constexpr int kMaxHeads = 8 * kMaxSplitChunks;
 constexpr float kRescaleSlack = 8.f;     // log2 headroom of the softmax reference maximum
 constexpr int kNtMinUnits = 256;         // (query, KV head) units from which K/V loads are non-temporal
 

@@ -27,6 +27,7 @@
 namespace qsa {
 
 constexpr int kCandCap = 256;    // threshold-bin population ranked directly
+constexpr int kHotLanes = 8;     // first scores of a wave in the top bin that make it count that bin
 
 // Inside the fully unrolled per-element loops: a scheduling fence every 4
 // elements, so the compiler does not compute all E derived values before
@@ -399,28 +400,44 @@ __device__ __forceinline__ int select_core(const float (&sv)[E], const int nf, c
   uint32_t bins[kKeepBins ? E / 2 : 1];
   if (grid) {
     const float c0f = fresh_uniform(cgrid), inv0 = fresh_uniform(inv);
+    // A wave whose first scores land in the grid's top bin several times
+    // (the row's maximum and those within a bin width of it: a row with many
+    // blocks tied at the top) counts that bin per thread and adds it once,
+    // instead of one LDS atomic per score serialised on one word.  Other
+    // waves pay one ballot for the test.
+    uint32_t ntop = 0u;
+    const bool hot = !wave_empty && __popcll(__ballot(grid_bin1(QSA_X(0), c0f, inv0) == kRadixBins)) >= kHotLanes;
+// the histogram pass of one wave: HOT counts the top bin, FULL skips the test
+// for empty slots (bin 0)
+#define QSA_HIST_PASS(HOT, FULL)                                 \
+  _Pragma("unroll") for (int e = 0; e < E; ++e) {               \
+    const int b1 = grid_bin1(QSA_X(e), c0f, inv0);              \
+    const bool top = (HOT) && b1 == kRadixBins;                 \
+    if (HOT) ntop += top ? 1u : 0u;                             \
+    if (((FULL) || b1 > 0) && !top) atomicAdd(&hist_g[b1], 1u); \
+    if (kKeepBins) {                                            \
+      if (e & 1) bins[e >> 1] |= (uint32_t)b1 << 16;            \
+      else bins[e >> 1] = (uint32_t)b1;                         \
+    }                                                           \
+    sched_fence(e);                                             \
+  }
     if (wave_full) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int b1 = grid_bin1(QSA_X(e), c0f, inv0);
-        atomicAdd(&hist_g[b1], 1u);
-        if (kKeepBins) {
-          if (e & 1) bins[e >> 1] |= (uint32_t)b1 << 16;
-          else bins[e >> 1] = (uint32_t)b1;
-        }
-        sched_fence(e);
+      if (hot) {
+        QSA_HIST_PASS(true, true)
+      } else {
+        QSA_HIST_PASS(false, true)
       }
     } else if (!wave_empty) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int b1 = grid_bin1(QSA_X(e), c0f, inv0);
-        if (b1 > 0) atomicAdd(&hist_g[b1], 1u);
-        if (kKeepBins) {
-          if (e & 1) bins[e >> 1] |= (uint32_t)b1 << 16;
-          else bins[e >> 1] = (uint32_t)b1;
-        }
-        sched_fence(e);
+      if (hot) {
+        QSA_HIST_PASS(true, false)
+      } else {
+        QSA_HIST_PASS(false, false)
       }
+    }
+#undef QSA_HIST_PASS
+    if (hot) {
+      const uint32_t wtop = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(ntop), kWave - 1);
+      if (lane == 0) atomicAdd(&hist_g[kRadixBins], wtop);
     }
     for (int i = tid; i < kRadixBins; i += NT) hist0[kRadixBins + i] = 0u;
     __syncthreads();
@@ -738,16 +755,13 @@ __global__ __launch_bounds__(kSelectThreads) void select_slice_kernel(Meta m, co
                                                   (int)blockIdx.x, lr);
 }
 
-// Long rows, launch 2: one workgroup per query keeps the top k of the
-// query's candidate row and writes sel (and pos).
-template <int E, int kPosOut>
-__global__ __launch_bounds__(kSelectThreads) void select_cand_kernel(Meta m, int k, int32_t* __restrict__ sel,
-                                                                     int32_t* __restrict__ n_sel,
-                                                                     int32_t* __restrict__ pos,
-                                                                     int32_t* __restrict__ n_pos, int width,
-                                                                     LongRows lr) {
-  select_row<E, kSelectThreads, kPosOut, kRowCand>(m, nullptr, 0, k, sel, n_sel, pos, n_pos, width,
-                                                      (int)blockIdx.x, lr);
+// Long rows, launch 2: one NT-thread workgroup per query keeps the top k of
+// the query's candidate row and writes sel (and pos).
+template <int E, int NT, int kPosOut>
+__global__ __launch_bounds__(NT) void select_cand_kernel(Meta m, int k, int32_t* __restrict__ sel,
+                                                         int32_t* __restrict__ n_sel, int32_t* __restrict__ pos,
+                                                         int32_t* __restrict__ n_pos, int width, LongRows lr) {
+  select_row<E, NT, kPosOut, kRowCand>(m, nullptr, 0, k, sel, n_sel, pos, n_pos, width, (int)blockIdx.x, lr);
 }
 
 // Position buffer from a selection: of the first min(n_sel, k) entries of
@@ -836,12 +850,15 @@ static void launch_select_t(const Meta& m, const float* scores, int64_t ld, int 
   const dim3 sgrid((unsigned)m.num_q, (unsigned)P);
   if (SB == 8192) select_slice_kernel<8><<<sgrid, kSelectThreads, 0, stream>>>(m, scores, ld, k, lr);
   else select_slice_kernel<16><<<sgrid, kSelectThreads, 0, stream>>>(m, scores, ld, k, lr);
-  if (lr.cstride <= 16 * kSelectThreads)
-    select_cand_kernel<16, kPosOut><<<m.num_q, kSelectThreads, 0, stream>>>(m, k, sel, n_sel, pos, n_pos, width,
-                                                                               lr);
-  else
-    select_cand_kernel<32, kPosOut><<<m.num_q, kSelectThreads, 0, stream>>>(m, k, sel, n_sel, pos, n_pos, width,
-                                                                               lr);
+  // the candidate step: 8 candidates per thread while they fit, on 512
+  // threads for the few candidates of up to 8 slices
+#define QSA_SELECT_CAND(EW, NTW) \
+  select_cand_kernel<EW, NTW, kPosOut><<<m.num_q, NTW, 0, stream>>>(m, k, sel, n_sel, pos, n_pos, width, lr)
+  if (lr.cstride <= 8 * 512) QSA_SELECT_CAND(8, 512);
+  else if (lr.cstride <= 8 * kSelectThreads) QSA_SELECT_CAND(8, kSelectThreads);
+  else if (lr.cstride <= 16 * kSelectThreads) QSA_SELECT_CAND(16, kSelectThreads);
+  else QSA_SELECT_CAND(32, kSelectThreads);
+#undef QSA_SELECT_CAND
 }
 
 size_t select_workspace_bytes(int num_q, int max_blocks) {

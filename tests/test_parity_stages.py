@@ -238,6 +238,41 @@ def test_select_small_k_long_rows(k, kind):
             assert np.array_equal(sel_h[i, :len(ref)], ref), (part[i], k)
             assert np.all(sel_h[i, len(ref):] == -1)
 
+@pytest.mark.parametrize("kind", ["ties", "normal"])
+def test_select_long_rows_many_queries(kind):
+    """A batch of 520 queries, three of them past 32,768 blocks (the two-step
+    selector runs for the whole batch: every short row goes through the slice
+    and candidate steps too), then its first 500 queries, on one workspace:
+    every row checked against the oracle, the control region zero after
+    each."""
+    need_gpu()
+    n = 520
+    rng = np.random.default_rng(611 + len(kind))
+    nfs = [int(x) for x in rng.integers(1, 3000, n)]
+    nfs[7], nfs[300], nfs[499] = 40000, 70001, 33000          # rows past 32,768 blocks
+    rows = _select_case(nfs, kind, seed=612 + len(kind))
+    ws = None
+    for part in (n, 500):
+        b = qsa.Batch(np.arange(part + 1), [4 * nf + 1 for nf in nfs[:part]], np.zeros(part), np.zeros(part))
+        if ws is None:
+            ws = torch.zeros(qsa.workspace_bytes(b, 1, 1), dtype=torch.uint8, device="cuda")
+        S = np.zeros((part, b.max_blocks), np.float32)
+        for i in range(part):
+            S[i, :nfs[i]] = rows[i]
+        sel = torch.full((part, qsa.TOPK), -7, dtype=torch.int32, device="cuda")
+        n_sel = torch.full((part,), -7, dtype=torch.int32, device="cuda")
+        say("qsa_select_topk long rows, queries", part, kind)
+        qsa.qsa_select_topk(b, torch.from_numpy(S).cuda(), sel, n_sel, workspace=ws)
+        torch.cuda.synchronize()
+        sel_h, n_h = sel.cpu().numpy(), n_sel.cpu().numpy()
+        for i in range(part):
+            ref = oracle.select_blocks(rows[i], qsa.TOPK)
+            assert n_h[i] == len(ref), (part, i, nfs[i])
+            assert np.array_equal(sel_h[i, :len(ref)], ref), (part, i, nfs[i])
+            assert np.all(sel_h[i, len(ref):] == -1)
+        assert int(ws[:CTL_BYTES].sum().item()) == 0
+
+
 @pytest.mark.parametrize("lens,nq", [([1, 2, 3, 4, 5, 17, 300, 2051, 2055, 9000, 12345, 20000],
                                        [1, 2, 3, 4, 1, 4, 2, 4, 3, 4, 1, 4]),
                                       ([140001, 33000, 5000], [4, 2, 1])])
