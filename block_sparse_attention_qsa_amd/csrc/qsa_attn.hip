@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   const int npos_given = p.n_pos[q];
   // never past the buffer (a row of run heads covers 4 positions an entry)
   const int npos = min(max(npos_given, 0), p.run_heads ? 4 * p.width : p.width);
-  const int slot0 = prow[0];
+  const int slot0 = max(prow[0], 0);       // masked loads read here (a row without positions holds -1)
 #ifdef QSA_DEBUG_CHECKS
   // the run rule over this workgroup's positions, and the length
   if (!p.run_heads) {

@@ -344,6 +344,56 @@ def test_sparse_attn_close(kv, hq, hkv, out_dtype):
             assert err.max() <= 2e-3 * np.abs(r).max()
 
 
+@pytest.mark.parametrize("hq,hkv,target_units,out_dtype", [(32, 4, 520, "f32"), (6, 3, 513, "bf16"), (8, 8, 512, "f32"),
+                                                          (16, 2, 600, "f32")])
+def test_sparse_attn_whole_units_fp8(hq, hkv, target_units, out_dtype):
+    """FP8 batches with at least 512 (query, KV head) units, so no unit is
+    split (the non-temporal, K-through-LDS kernel with its ping-pong
+    buffers): even and odd unit counts, mixed lengths (a few blocks to past
+    512 blocks, with partial blocks) and GQA groups of 8, 2 and 1, through
+    the stage call and through the decode (with and without positions
+    requested)."""
+    need_gpu()
+    rng = np.random.default_rng(900 + hq + hkv)
+    lens, nq = [], []
+    while sum(nq) * hkv < target_units:
+        lens.append(int(rng.integers(5, 14000)))
+        nq.append(int(rng.integers(1, 5)))
+    if target_units % 2 != (sum(nq) * hkv) % 2:    # the odd case keeps an odd unit count
+        lens.append(777)
+        nq.append(1)
+    w = make_custom(f"whole-{hq}-{hkv}", lens, nq, hq, hkv, kv_dtype="fp8_e4m3", seed=901 + hq)
+    say("qsa_sparse_attn whole units", w.name, "queries", w.num_q, "units", w.num_q * hkv)
+    assert w.num_q * hkv >= 512 and (w.num_q * hkv) % 2 == target_units % 2
+    ref = oracle_decode(w, want_scores=False)
+    dev = upload(w)
+    b = batch_of(w)
+    tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    ws = qsa.alloc_workspace(b, hq, hkv)
+
+    def check(out):
+        got = out.float().cpu().numpy().astype(np.float64)
+        if out_dtype == "f32":
+            assert_out_close(got, ref["out"])
+        else:
+            r = ref["out"]
+            err = np.abs(got - r) - 2.0 ** -8 * np.abs(r)
+            assert err.max() <= 2e-3 * np.abs(r).max()
+
+    out = torch.full((w.num_q, hq, 128), float("nan"), dtype=tdt, device="cuda")
+    qsa.qsa_sparse_attn(b, dev["q"], dev["k_cache"], dev["v_cache"], torch.from_numpy(ref["pos"]).cuda(),
+                        torch.from_numpy(ref["n_pos"]).cuda(), out, k_scale=dev["k_scale"], v_scale=dev["v_scale"],
+                        sm_scale=SM_SCALE, workspace=ws)
+    torch.cuda.synchronize()
+    check(out)
+    if out_dtype == "f32":
+        got = run_decode(w, dev, ws=ws)
+        assert_selection_equal(got, ref)
+        assert_out_close(got["out"], ref["out"])
+        lean = run_decode(w, dev, ws=ws, debug=False)
+        assert np.array_equal(lean["out"].view(np.uint64), got["out"].view(np.uint64))
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
 def test_sparse_attn_permuted_runs(kv):
     """A valid position buffer whose 4-slot runs come in a shuffled order (the
