@@ -474,6 +474,23 @@ def test_decode_edge_lengths_dense_equivalence():
             np.testing.assert_allclose(got["out"][qi], np.repeat(v, 8, axis=0), rtol=1e-6, atol=1e-6)
 
 
+def test_decode_no_full_blocks():
+    """Batches where no request has a full 4-token block (max_blocks = 0: no
+    scoring launch, nothing to select): every query attends over its partial
+    block only, as dense attention over its 1-3 tokens; also a single token."""
+    need_gpu()
+    for lens, nq, kv in (([1, 2, 3, 3, 2], [1, 2, 3, 1, 2], "bf16"), ([3, 1], [3, 1], "fp8_e4m3"), ([1], [1], "bf16")):
+        w = make_custom("nofull", lens, nq, 8, 2, kv_dtype=kv, seed=811 + len(lens))
+        say("qsa_decode without full blocks", lens, nq, kv)
+        assert batch_of(w).max_blocks == 0
+        ref = oracle_decode(w, want_scores=False)
+        got = run_decode(w)
+        assert_selection_equal(got, ref)
+        assert np.all(got["n_pos"] == np.array([int(x) for x in ref["n_pos"]]))
+        assert_out_close(got["out"], ref["out"])
+        assert_lean_decode_same(w, got)
+
+
 def test_decode_small_k():
     need_gpu()
     w = _mixed_workload(seed=801)
