@@ -39,7 +39,7 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 constexpr int64_t kMaxScoreLd = int64_t(1) << 26;
 
 struct WsLayout {
-  size_t counters, partials, attn_end, scores, sel, n_sel, pos, n_pos, msel, total;
+  size_t counters, plan, partials, attn_end, scores, sel, n_sel, pos, n_pos, msel, total;
 };
 
 // Row stride of the workspace score buffer: a multiple of 4 floats so that
@@ -52,6 +52,7 @@ WsLayout ws_layout(int num_q, int max_blocks, int hq, int hkv, int k) {
   size_t off = 0;
   // fixed control region first (see kCtlBytes), whatever the geometry
   w.counters = off; off += align_up(qsa::kCtlBytes);
+  w.plan = off; off += align_up(qsa::attn_plan_bytes(num_q, hkv, width));
   w.partials = off; off += align_up(qsa::attn_partial_bytes(num_q, hkv, hq / hkv, width));
   w.attn_end = off;
   w.scores = off; off += align_up((size_t)num_q * (size_t)score_ld(max_blocks) * sizeof(float));
@@ -182,8 +183,14 @@ qsa_status decode_body(const qsa_batch* batch, const void* idx_q, const void* ck
   // slot per 4-slot run (a quarter of the position rows) instead.
   const bool run_heads = pos_opt == nullptr;
   QSA_TRY(launched(qsa::launch_score(m, idx_q, ckeys, scores, ld, stream)));
+  // a ragged batch: the selection launch also writes the attention's work list
+  qsa::AttnPlan plan{nullptr, num_kv_heads, k, 0, nullptr, 0};
+  if (qsa::attn_ragged(m.num_req, m.num_q, num_kv_heads)) {
+    plan.words = reinterpret_cast<int32_t*>(base + w.plan);
+    plan.cps_min = qsa::attn_split(m.num_q, num_kv_heads, width, true).chunks_per_split;
+  }
   QSA_TRY(launched(qsa::launch_select(m, scores, ld, k, sel, n_sel, pos, n_pos, run_heads ? k + 1 : width, run_heads,
-                                      base + w.msel, stream)));
+                                      base + w.msel, plan, stream)));
   qsa::AttnArgs a;
   a.q = q;
   a.k_cache = k_cache;
@@ -202,6 +209,7 @@ qsa_status decode_body(const qsa_batch* batch, const void* idx_q, const void* ck
   a.out_bf16 = out_dtype == QSA_OUT_BF16;
   a.partials = reinterpret_cast<float*>(base + w.partials);
   a.counters = reinterpret_cast<uint32_t*>(base + w.counters);
+  a.plan = plan.words;
   a.err = m.err;
   return launched(qsa::launch_attn(m, a, stream));
 }
@@ -302,7 +310,8 @@ qsa_status qsa_select_topk(const qsa_batch* batch, const float* scores, int64_t 
   QSA_TRY(check_ws(ws, ws_bytes, cand ? qsa::kCtlBytes + cand : 0));
   return launched(qsa::launch_select(meta_of(batch), scores, ld, k, sel, n_sel, nullptr, nullptr,
                                      QSA_BLOCK * k + QSA_BLOCK - 1, false,
-                                     cand ? static_cast<char*>(ws) + qsa::kCtlBytes : nullptr, stream));
+                                     cand ? static_cast<char*>(ws) + qsa::kCtlBytes : nullptr, qsa::AttnPlan{nullptr, 0, 0, 0, nullptr, 0},
+                                     stream));
 }
 
 qsa_status qsa_select_positions(const qsa_batch* batch, const float* scores, int64_t ld, int32_t k, int32_t* sel,
@@ -316,7 +325,8 @@ qsa_status qsa_select_positions(const qsa_batch* batch, const float* scores, int
   QSA_TRY(check_ws(ws, ws_bytes, cand ? qsa::kCtlBytes + cand : 0));
   return launched(qsa::launch_select(meta_of(batch), scores, ld, k, sel, n_sel, pos, n_pos,
                                      QSA_BLOCK * k + QSA_BLOCK - 1, false,
-                                     cand ? static_cast<char*>(ws) + qsa::kCtlBytes : nullptr, stream));
+                                     cand ? static_cast<char*>(ws) + qsa::kCtlBytes : nullptr, qsa::AttnPlan{nullptr, 0, 0, 0, nullptr, 0},
+                                     stream));
 }
 
 qsa_status qsa_build_index(const qsa_batch* batch, const int32_t* sel, const int32_t* n_sel, int32_t k,
@@ -362,8 +372,17 @@ qsa_status qsa_sparse_attn(const qsa_batch* batch, const void* q, const void* k_
   a.out_bf16 = out_dtype == QSA_OUT_BF16;
   a.partials = reinterpret_cast<float*>(base + w.partials);
   a.counters = reinterpret_cast<uint32_t*>(base + w.counters);
+  a.plan = nullptr;
   a.err = device_error_word();
-  return launched(qsa::launch_attn(meta_of(batch), a, stream));
+  const qsa::Meta m = meta_of(batch);
+  if (qsa::attn_ragged(m.num_req, m.num_q, num_kv_heads)) {
+    // a ragged batch: a work list from the given position counts first
+    qsa::AttnPlan plan{reinterpret_cast<int32_t*>(base + w.plan), num_kv_heads, k,
+                       qsa::attn_split(m.num_q, num_kv_heads, width, true).chunks_per_split, n_pos, width};
+    QSA_TRY(launched(qsa::launch_attn_plan(m, plan, stream)));
+    a.plan = plan.words;
+  }
+  return launched(qsa::launch_attn(m, a, stream));
 }
 
 qsa_status qsa_compress_keys(const qsa_batch* batch, const int32_t* prev_len, const void* tok_keys, void* ckeys,

@@ -53,11 +53,7 @@ __device__ __forceinline__ float load_coherent_f32(__amdgpu_buffer_rsrc_t r, int
 __device__ __forceinline__ void store_coherent_f32(__amdgpu_buffer_rsrc_t r, int float_off, float v) {
   __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, float_off * 4, 0, kCpolDevice);
 }
-// Block heads of one split: 8 per chunk, for the most chunks a split takes
-// (a whole 2,051-position row, its 65 chunks rounded up to whole 4-chunk
-// steps).
-constexpr int kMaxSplitChunks = ((QSA_WIDTH + kChunk - 1) / kChunk + kAttnWaves - 1) / kAttnWaves * kAttnWaves;
-constexpr int kMaxHeads = 8 * kMaxSplitChunks;
+constexpr int kMaxHeads = 8 * kMaxSplitChunks;   // block heads of one split (8 per chunk)
 constexpr float kRescaleSlack = 8.f;     // log2 headroom of the softmax reference maximum
 constexpr int kNtMinUnits = 256;         // (query, KV head) units from which K/V loads are non-temporal
 
@@ -73,10 +69,11 @@ struct AttnParams {
   float* part;
   uint32_t* counters;
   uint32_t* err;            // error word (QSA_ERROR_* bits), or nullptr
-  int width, num_q_heads, num_kv_heads, group;
+  int num_q, width, num_q_heads, num_kv_heads, group;
   int run_heads;            // pos holds one slot per 4-slot run (rows of width entries)
   float sm_scale_log2;
   int splits, cps;
+  const int32_t* plan;      // the ragged batch's work list (AttnPlan), or nullptr: the grid is (q, KV head, split)
 };
 
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
@@ -395,7 +392,8 @@ constexpr int kWaitLds = 0xC07F;
 
 constexpr int kAttnThreads = 64 * kAttnWaves;
 
-template <bool kFp8, bool kOutBf16, bool kNt>
+
+template <bool kFp8, bool kOutBf16, bool kNt, bool kPlan = false>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   constexpr int D = QSA_HEAD_DIM;
   constexpr int EB = kFp8 ? 1 : 2;            // bytes per KV element
@@ -415,20 +413,39 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   // the grid has more workgroups than the chip has CUs it is those nearly
   // empty workgroups that share a CU with another.
   const int Hkv = p.num_kv_heads;
-  const int q = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  int q = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
   const int j = lane & 15, kg = lane >> 4;
   const int G = p.group;
   const bool hvalid = j < G;
   const int Hq = p.num_q_heads;
+  // Chunks per split and this unit's splits: fixed by the launch, or, for a
+  // ragged batch, item blockIdx.x of the work list the selection wrote (the
+  // 1-D grid's workgroups past the list leave here).
+  int cps = p.cps, S = p.splits;
+  if (kPlan) {
+    const int w = blockIdx.x;
+    const int items = p.plan[0];
+    cps = min(max(p.plan[1], 1), kMaxSplitChunks);
+    const uint32_t e = (uint32_t)p.plan[kPlanHeader + w];   // the grid never exceeds the list's room
+    if (w >= items) return;
+    q = (int)(e & 0xFFFu);
+    g = (int)((e >> 12) & 0x7Fu);
+    s = (int)((e >> 19) & 0x1Fu);
+    S = (int)((e >> 24) & 0x1Fu);
+    q = min(q, p.num_q - 1);
+    g = min(g, Hkv - 1);
+    S = min(max(S, 1), p.splits);
+    s = min(s, S - 1);
+  }
   const int32_t* prow = p.pos + (int64_t)q * p.width;
-  const int c0 = s * p.cps;                 // first chunk of this workgroup's split
+  const int c0 = s * cps;                   // first chunk of this workgroup's split
   const int cfirst = c0 + wave;
 
   // Prologue: the block heads of the split go to LDS, the query rows to
   // registers, with the valid length and the first slot; every load is
   // issued before any is waited for (one memory round trip).
-  for (int h = tid; h < 8 * p.cps; h += kAttnThreads) {
+  for (int h = tid; h < 8 * cps; h += kAttnThreads) {
     const int run = 8 * c0 + h;
     const int i = p.run_heads ? run : 4 * run;
     heads_s[h] = i < p.width ? prow[i] : 0;
@@ -442,7 +459,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   if (!p.run_heads) {
     if (tid == 0 && s == 0 && g == 0)
       QSA_DCHECK(p.err, npos_given >= 1 && npos_given <= p.width, QSA_ERROR_BAD_POSITIONS);
-    for (int i = 32 * c0 + tid; i < min(32 * (c0 + p.cps), min(npos, p.width)); i += kAttnThreads)
+    for (int i = 32 * c0 + tid; i < min(32 * (c0 + cps), min(npos, p.width)); i += kAttnThreads)
       QSA_DCHECK(p.err, prow[i] == prow[i & ~3] + (i & 3), QSA_ERROR_BAD_POSITIONS);
   }
 #endif
@@ -462,7 +479,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   const uint8_t* kbase = p.kc + (int64_t)g * D * EB;
   const uint8_t* vbase = p.vc + (int64_t)g * D * EB;
   const int nchunks = (npos + kChunk - 1) / kChunk;
-  const int c_end = min(c0 + p.cps, nchunks);
+  const int c_end = min(c0 + cps, nchunks);
+  // a work list sized the unit's splits from the metadata; the selection's
+  // count must fit them
+  if (kPlan && tid == 0 && s == 0) QSA_DCHECK(p.err, nchunks <= S * cps, QSA_ERROR_BAD_POSITIONS);
   __syncthreads();
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -488,12 +508,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
     constexpr int kIssueOps = KL::kLoads + 8;
     ChunkRaw<kFp8, kKL> ca, cb;
     const int nl = cfirst < c_end ? npos : 0;
-    issue_chunk<kFp8, kNt, kKL>(ca, kbuf0, lds_heads<kFp8, kKL>(heads_s, cfirst - c0, p.cps, lane, j, kg),
+    issue_chunk<kFp8, kNt, kKL>(ca, kbuf0, lds_heads<kFp8, kKL>(heads_s, cfirst - c0, cps, lane, j, kg),
                                 cfirst * kChunk, nl, slot0, kbase, vbase, row_stride, lane, j, kg);
     __builtin_amdgcn_sched_barrier(0);
     for (int c = cfirst; c < c_end; c += 2 * kAttnWaves) {
       const int cn = c + kAttnWaves;
-      issue_chunk<kFp8, kNt, kKL>(cb, kbuf1, lds_heads<kFp8, kKL>(heads_s, cn - c0, p.cps, lane, j, kg),
+      issue_chunk<kFp8, kNt, kKL>(cb, kbuf1, lds_heads<kFp8, kKL>(heads_s, cn - c0, cps, lane, j, kg),
                                   cn * kChunk, cn < c_end ? npos : 0, slot0, kbase, vbase, row_stride, lane, j, kg);
       __builtin_amdgcn_sched_barrier(0);
       if (kKL) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kIssueOps));
@@ -502,7 +522,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
       __builtin_amdgcn_sched_barrier(0);
       if (cn >= c_end) break;
       const int cnn = cn + kAttnWaves;
-      issue_chunk<kFp8, kNt, kKL>(ca, kbuf0, lds_heads<kFp8, kKL>(heads_s, cnn - c0, p.cps, lane, j, kg),
+      issue_chunk<kFp8, kNt, kKL>(ca, kbuf0, lds_heads<kFp8, kKL>(heads_s, cnn - c0, cps, lane, j, kg),
                                   cnn * kChunk, cnn < c_end ? npos : 0, slot0, kbase, vbase, row_stride, lane, j,
                                   kg);
       __builtin_amdgcn_sched_barrier(0);
@@ -514,7 +534,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   } else {
     for (int c = cfirst; c < c_end; c += kAttnWaves) {
       ChunkRaw<kFp8, kKL> cur;
-      issue_chunk<kFp8, kNt, kKL>(cur, kbuf0, lds_heads<kFp8, kKL>(heads_s, c - c0, p.cps, lane, j, kg), c * kChunk,
+      issue_chunk<kFp8, kNt, kKL>(cur, kbuf0, lds_heads<kFp8, kKL>(heads_s, c - c0, cps, lane, j, kg), c * kChunk,
                                   npos, slot0, kbase, vbase, row_stride, lane, j, kg);
       if (kKL) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       compute_chunk<kFp8, kKL>(cur, kbuf0, qb, sl2, m_run, l_run, o, j, kg);
@@ -545,7 +565,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   __syncthreads();
 
   const int nout = G * D;
-  if (p.splits == 1) {
+  if (S == 1) {
     // 4 consecutive outputs of one head per thread
     for (int v4 = tid; v4 < nout / 4; v4 += kAttnThreads) {
       const int hh = (4 * v4) / D, d = (4 * v4) % D;
@@ -603,10 +623,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   __builtin_amdgcn_s_waitcnt(0);     // this thread's stores have reached the coherence point
   __syncthreads();
   uint32_t* const ctr = p.counters + (q * Hkv + g) * kCounterStride;
-  const int S = p.splits;
   if (tid == 0) {
     const uint32_t ticket = atomicAdd(ctr, 1u);
-    s_last = ticket == (uint32_t)(p.splits - 1);
+    s_last = ticket == (uint32_t)(S - 1);
   }
   __syncthreads();
   if (!s_last) return;
@@ -651,8 +670,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
   if (tid == 0) ctr[0] = 0u;
 }
 
+size_t attn_plan_bytes(int num_q, int num_kv_heads, int width) {
+  if (num_q * num_kv_heads >= kAttnTargetWgs) return 0;
+  const AttnSplit sp = attn_split(num_q, num_kv_heads, width, true);
+  return (size_t)(kPlanHeader + (int64_t)num_q * num_kv_heads * sp.splits) * sizeof(int32_t);
+}
+
 size_t attn_partial_bytes(int num_q, int num_kv_heads, int group, int width) {
-  const AttnSplit sp = attn_split(num_q, num_kv_heads, width);
+  // sized for the ragged geometry whenever a batch could take it (it has at
+  // least the splits of the uniform one)
+  const AttnSplit sp = attn_split(num_q, num_kv_heads, width, num_q * num_kv_heads < kAttnTargetWgs);
   if (sp.splits <= 1) return 0;
   return (size_t)num_q * num_kv_heads * sp.splits * (group * QSA_HEAD_DIM + 32) * sizeof(float);
 }
@@ -660,7 +687,9 @@ size_t attn_partial_bytes(int num_q, int num_kv_heads, int group, int width) {
 hipError_t launch_attn(const Meta& m, const AttnArgs& a, hipStream_t stream) {
   // the split geometry follows the positions (4 per run head)
   const int pos_width = a.run_heads ? QSA_BLOCK * (a.width - 1) + QSA_BLOCK - 1 : a.width;
-  const AttnSplit sp = attn_split(m.num_q, a.num_kv_heads, pos_width);
+  // the ragged geometry only with a work list (qsa_decode on a ragged batch)
+  const bool ragged = a.plan != nullptr && attn_ragged(m.num_req, m.num_q, a.num_kv_heads);
+  const AttnSplit sp = attn_split(m.num_q, a.num_kv_heads, pos_width, ragged);
   AttnParams p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.kc = static_cast<const uint8_t*>(a.k_cache);
@@ -681,15 +710,22 @@ hipError_t launch_attn(const Meta& m, const AttnArgs& a, hipStream_t stream) {
   p.splits = sp.splits;
   p.cps = sp.chunks_per_split;
   p.err = a.err;
-  const dim3 grid((unsigned)m.num_q, (unsigned)a.num_kv_heads, (unsigned)sp.splits);
+  p.plan = ragged ? a.plan : nullptr;
+  p.num_q = m.num_q;
+  // a ragged batch with a work list: one workgroup per item, as many as the
+  // list can hold (those past its length leave at once)
+  const dim3 grid = p.plan != nullptr ? dim3((unsigned)(m.num_q * a.num_kv_heads * sp.splits))
+                                      : dim3((unsigned)m.num_q, (unsigned)a.num_kv_heads, (unsigned)sp.splits);
   // Large batches stream K/V with non-temporal loads (measured faster once
   // the (query, KV head) units alone fill the chip); small ones keep the
   // default policy (faster there).
   const bool nt = (int64_t)m.num_q * a.num_kv_heads >= kNtMinUnits;
-#define QSA_ATTN_LAUNCH(F8, OB)                                              \
-  do {                                                                        \
-    if (nt) attn_kernel<F8, OB, true><<<grid, kAttnThreads, 0, stream>>>(p);           \
-    else attn_kernel<F8, OB, false><<<grid, kAttnThreads, 0, stream>>>(p);             \
+#define QSA_ATTN_LAUNCH(F8, OB)                                                       \
+  do {                                                                                 \
+    if (p.plan && nt) attn_kernel<F8, OB, true, true><<<grid, kAttnThreads, 0, stream>>>(p);   \
+    else if (p.plan) attn_kernel<F8, OB, false, true><<<grid, kAttnThreads, 0, stream>>>(p);  \
+    else if (nt) attn_kernel<F8, OB, true><<<grid, kAttnThreads, 0, stream>>>(p);              \
+    else attn_kernel<F8, OB, false><<<grid, kAttnThreads, 0, stream>>>(p);                     \
   } while (0)
   if (a.kv_fp8) {
     if (a.out_bf16) QSA_ATTN_LAUNCH(true, true);

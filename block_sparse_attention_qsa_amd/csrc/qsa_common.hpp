@@ -160,15 +160,25 @@ constexpr int kLongRowBlocks = 32768;
 
 // Attention split geometry shared by the launcher and the workspace sizing.
 struct AttnSplit {
-  int splits;            // workgroups per (query, KV head)
-  int chunks_per_split;  // 32-position chunks per workgroup (multiple of kAttnWaves)
+  int splits;            // workgroups per (query, KV head): the grid's third dimension
+  int chunks_per_split;  // 32-position chunks per workgroup (multiple of kAttnWaves); with
+                         // ragged, the least the kernel takes
 };
 
-__host__ __device__ inline AttnSplit attn_split(int num_q, int num_kv_heads, int width) {
+// ragged = false: every unit is split alike, into enough workgroups that
+// about kAttnTargetWgs are resident (two 4-wave workgroups per CU).
+// ragged = true (batches of several requests, whose units' position counts
+// differ): room for up to twice as many splits per unit; the work list
+// (AttnPlan) sizes the splits from the batch's total positions, so that a
+// long unit gets several workgroups and a short one a single one, and the
+// grid's workgroups past the list leave at once.  Only while the units
+// number fewer than kAttnTargetWgs (their arrival counters must fit the
+// control region).
+__host__ __device__ inline AttnSplit attn_split(int num_q, int num_kv_heads, int width, bool ragged = false) {
   const int chunks = (width + kChunk - 1) / kChunk;
   const int units = num_q * num_kv_heads;
-  // two 4-wave workgroups per CU are resident at once
-  int splits = units >= kAttnTargetWgs ? 1 : (kAttnTargetWgs + units - 1) / units;
+  const int target = ragged ? 2 * kAttnTargetWgs : kAttnTargetWgs;
+  int splits = units >= kAttnTargetWgs ? 1 : (target + units - 1) / units;
   int max_splits = (chunks + kAttnWaves - 1) / kAttnWaves;   // <= kMaxSplits for width <= QSA_WIDTH
   if (splits > max_splits) splits = max_splits;
   if (splits < 1) splits = 1;
@@ -179,6 +189,35 @@ __host__ __device__ inline AttnSplit attn_split(int num_q, int num_kv_heads, int
   a.splits = splits;
   a.chunks_per_split = cps;
   return a;
+}
+
+// The most chunks one attention split takes: a whole 2,051-position row,
+// its 65 chunks rounded up to whole 4-chunk steps.
+constexpr int kMaxSplitChunks = ((QSA_WIDTH + kChunk - 1) / kChunk + kAttnWaves - 1) / kAttnWaves * kAttnWaves;
+
+// Work list of the attention for a ragged batch inside qsa_decode, written
+// by one extra workgroup of the selection launch: kPlanHeader header words
+// ([0] items, [1] chunks per split), then one word per item (query, KV
+// head, split, the unit's splits): every split of the full chunk count
+// first, then each unit's last, shorter split, longest first (a longest-
+// first list: the long work starts first, short work fills in at the end).
+// Attention workgroup w takes item w.
+constexpr int kPlanHeader = 16;
+__host__ __device__ inline uint32_t plan_item(int q, int g, int s, int S) {
+  return (uint32_t)q | ((uint32_t)g << 12) | ((uint32_t)s << 19) | ((uint32_t)S << 24);
+}
+struct AttnPlan {
+  int32_t* words;         // header + items (workspace); nullptr: no plan
+  int num_kv_heads;
+  int k;                  // selection size (positions of a query: 4 min(L/4, k) + L mod 4)
+  int cps_min;            // least chunks per split (so no unit needs more splits than the grid has)
+  const int32_t* n_pos;   // the position counts to plan for (clamped to pos_cap), or nullptr: from the metadata
+  int pos_cap;
+};
+
+// Whether a batch takes the ragged split geometry (see attn_split).
+__host__ __device__ inline bool attn_ragged(int num_req, int num_q, int num_kv_heads) {
+  return num_req > 1 && num_q * num_kv_heads < kAttnTargetWgs;
 }
 
 }  // namespace qsa

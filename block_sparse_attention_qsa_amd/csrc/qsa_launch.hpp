@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "qsa.h"
+#include "qsa_common.hpp"
 
 namespace qsa {
 
@@ -63,6 +64,7 @@ struct AttnArgs {
   int out_bf16;
   float* partials;          // split partial results (workspace)
   uint32_t* counters;       // [num_q][Hkv] split arrival counters (workspace, zero)
+  const int32_t* plan;      // the work list the selection wrote for a ragged batch, or nullptr
   uint32_t* err;            // error word (QSA_ERROR_* bits) or nullptr
 };
 
@@ -74,10 +76,15 @@ hipError_t launch_score(const Meta& m, const void* idx_q, const void* ckeys, flo
 // width >= k + 1 entries).  Rows longer than 32,768 blocks keep their slices'
 // candidates in select_workspace_bytes() of workspace at ws (256-byte aligned;
 // no initial contents needed).
+// With plan.words, one extra workgroup writes the attention's work list for
+// a ragged batch there (AttnPlan; attn_plan_bytes()).
 hipError_t launch_select(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel,
                          int32_t* n_sel, int32_t* pos, int32_t* n_pos, int width, bool run_heads, void* ws,
-                         hipStream_t stream);
+                         const AttnPlan& plan, hipStream_t stream);
 size_t select_workspace_bytes(int num_q, int max_blocks);
+// The attention's work list for a ragged batch of at most 511 queries, from
+// plan.n_pos, in a launch of its own.
+hipError_t launch_attn_plan(const Meta& m, const AttnPlan& plan, hipStream_t stream);
 hipError_t launch_build_index(const Meta& m, const int32_t* sel, const int32_t* n_sel, int k, int32_t* pos,
                               int32_t* n_pos, int width, hipStream_t stream);
 hipError_t launch_attn(const Meta& m, const AttnArgs& a, hipStream_t stream);
@@ -87,6 +94,9 @@ hipError_t launch_compress_keys(const Meta& m, const int32_t* prev_len, const vo
 // Zero-fills bytes (a multiple of 16) at p with a kernel on stream.
 hipError_t launch_zero_fill(void* p, size_t bytes, hipStream_t stream);
 
+// Bytes of the attention's work list for a ragged batch of this geometry
+// (0 when the batch could not take one).
+size_t attn_plan_bytes(int num_q, int num_kv_heads, int width);
 // Bytes of split partials the attention needs for this geometry.
 size_t attn_partial_bytes(int num_q, int num_kv_heads, int group, int width);
 

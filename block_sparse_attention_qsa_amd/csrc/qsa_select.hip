@@ -737,11 +737,87 @@ __device__ __forceinline__ void select_row(const Meta& m, const float* __restric
   write_selection<NT, kPosOut>(sel_s, ns, k, nfq, pl, m, r, kv0, paged, sel_row, pos_row, width, n_sel, n_pos, q);
 }
 
-template <int E, int NT, int kPosOut>
+// The attention's work list for a ragged batch (AttnPlan), built by one
+// NT-thread workgroup (NT > num_q): an extra workgroup of the selection
+// launch inside qsa_decode, or a launch of its own before the stage
+// attention.  Query q has n positions - 4 min(nf, k) + L mod 4 from the
+// metadata (what the selection in the same launch writes as n_pos), or the
+// given counts - and nch = ceil(n / 32) chunks; the chunks per split cps spread the
+// batch's chunks over kAttnTargetWgs workgroups in whole 4-chunk steps.  Each
+// (query, KV head) unit gets nch / cps full splits and, when the division
+// leaves a rest, one shorter split; full splits come first in the list, the
+// shorter ones after them by decreasing size (a counting sort; ties in any
+// order - each item's arithmetic, and the order of its unit's merge, do not
+// depend on where it sits in the list).
+template <int NT>
+__device__ __forceinline__ void build_attn_plan(const Meta& m, const AttnPlan& pl) {
+  __shared__ uint32_t scan_s[NT / kWave];
+  __shared__ uint32_t hist_s[kMaxSplitChunks + 1], base_s[kMaxSplitChunks + 1];
+  const int tid = threadIdx.x;
+  const int H = pl.num_kv_heads;
+  for (int i = tid; i <= kMaxSplitChunks; i += NT) hist_s[i] = 0u;
+  int nch = 0;
+  if (tid < m.num_q) {
+    int n;
+    if (pl.n_pos != nullptr) {
+      n = min(max(pl.n_pos[tid], 0), pl.pos_cap);
+    } else {
+      const int r = request_of(m.q_start, m.num_req, tid);
+      const int qs = m.q_start[r];
+      const int nq = m.q_start[r + 1] - qs;
+      const int L = max(m.seq_len[r] - nq + 1 + (tid - qs), 0);
+      const int nf = min(L >> 2, m.max_blocks);
+      n = 4 * min(nf, pl.k) + (L & 3);
+    }
+    nch = (n + kChunk - 1) / kChunk;
+  }
+  uint32_t tot;
+  block_exclusive_scan<NT>((uint32_t)nch, scan_s, &tot);
+  __syncthreads();                        // scan_s is read by every wave before it is reused
+  int cps = (int)(((uint64_t)tot * (uint32_t)H + kAttnTargetWgs - 1) / kAttnTargetWgs);
+  cps = (cps + kAttnWaves - 1) / kAttnWaves * kAttnWaves;
+  cps = min(max(cps, pl.cps_min), kMaxSplitChunks);
+  const int f = tid < m.num_q ? nch / cps : 0;
+  const int rest = tid < m.num_q ? nch - f * cps : 0;
+  const bool part = tid < m.num_q && (rest > 0 || nch == 0);   // a unit without positions still gets one item
+  const int S = f + (part ? 1 : 0);
+  uint32_t nfull;
+  const uint32_t fbefore = block_exclusive_scan<NT>((uint32_t)f, scan_s, &nfull);
+  if (part) atomicAdd(&hist_s[rest], 1u);
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t run = 0u;
+    for (int c = kMaxSplitChunks; c >= 0; --c) {   // longest rest first
+      base_s[c] = run;
+      run += hist_s[c];
+    }
+    pl.words[0] = (int32_t)((nfull + run) * (uint32_t)H);
+    pl.words[1] = cps;
+  }
+  __syncthreads();
+  uint32_t* items = reinterpret_cast<uint32_t*>(pl.words + kPlanHeader);
+  if (tid < m.num_q) {
+    for (int s = 0; s < f; ++s)
+      for (int g = 0; g < H; ++g) items[(fbefore + s) * H + g] = plan_item(tid, g, s, S);
+    if (part) {
+      const uint32_t slot = nfull + atomicAdd(&base_s[rest], 1u);   // base_s now serves as the cursor
+      for (int g = 0; g < H; ++g) items[slot * H + g] = plan_item(tid, g, f, S);
+    }
+  }
+}
+
+// The work list alone (the stage attention on a ragged batch).
+__global__ __launch_bounds__(512) void attn_plan_kernel(Meta m, AttnPlan plan) { build_attn_plan<512>(m, plan); }
+
+template <int E, int NT, int kPosOut, bool kPlan = false>
 __global__ __launch_bounds__(NT) void select_reg_kernel(Meta m, const float* __restrict__ scores, int64_t ld,
                                                         int k, int32_t* __restrict__ sel,
                                                         int32_t* __restrict__ n_sel, int32_t* __restrict__ pos,
-                                                        int32_t* __restrict__ n_pos, int width) {
+                                                        int32_t* __restrict__ n_pos, int width, AttnPlan plan) {
+  if (kPlan && (int)blockIdx.x == m.num_q) {   // the extra workgroup: the attention's work list
+    build_attn_plan<NT>(m, plan);
+    return;
+  }
   select_row<E, NT, kPosOut>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, (int)blockIdx.x, LongRows{});
 }
 
@@ -757,10 +833,15 @@ __global__ __launch_bounds__(kSelectThreads) void select_slice_kernel(Meta m, co
 
 // Long rows, launch 2: one NT-thread workgroup per query keeps the top k of
 // the query's candidate row and writes sel (and pos).
-template <int E, int NT, int kPosOut>
+template <int E, int NT, int kPosOut, bool kPlan = false>
 __global__ __launch_bounds__(NT) void select_cand_kernel(Meta m, int k, int32_t* __restrict__ sel,
                                                          int32_t* __restrict__ n_sel, int32_t* __restrict__ pos,
-                                                         int32_t* __restrict__ n_pos, int width, LongRows lr) {
+                                                         int32_t* __restrict__ n_pos, int width, LongRows lr,
+                                                         AttnPlan plan) {
+  if (kPlan && (int)blockIdx.x == m.num_q) {   // the extra workgroup: the attention's work list
+    build_attn_plan<NT>(m, plan);
+    return;
+  }
   select_row<E, NT, kPosOut, kRowCand>(m, nullptr, 0, k, sel, n_sel, pos, n_pos, width, (int)blockIdx.x, lr);
 }
 
@@ -814,16 +895,25 @@ __global__ __launch_bounds__(256) void build_index_kernel(Meta m, const int32_t*
 
 template <int kPosOut>
 static void launch_select_t(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel, int32_t* n_sel,
-                            int32_t* pos, int32_t* n_pos, int width, uint32_t* ms_ws, hipStream_t stream) {
+                            int32_t* pos, int32_t* n_pos, int width, uint32_t* ms_ws, const AttnPlan& plan,
+                            hipStream_t stream) {
+  // one more workgroup than queries builds the attention's work list
+  const unsigned nwg = (unsigned)m.num_q + (plan.words != nullptr ? 1u : 0u);
   // Rows up to 16,384 blocks: the narrowest even segment that covers the
   // longest row (at least 8 scores per thread), so that the busiest SIMD of
   // the workgroup runs as few score slots as the row needs.
   if (m.max_blocks <= 16384) {
     const int e = max(8, ((m.max_blocks + kSelectThreads - 1) / kSelectThreads + 1) & ~1);
-    const dim3 g((unsigned)m.num_q);
-#define QSA_SELECT_REG(EW)                                                                               \
-  select_reg_kernel<EW, kSelectThreads, kPosOut><<<g, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, \
-                                                                                     n_sel, pos, n_pos, width)
+    const dim3 g(nwg);
+#define QSA_SELECT_REG(EW)                                                                                    \
+  do {                                                                                                         \
+    if (plan.words)                                                                                            \
+      select_reg_kernel<EW, kSelectThreads, kPosOut, true>                                                    \
+          <<<g, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, plan);          \
+    else                                                                                                       \
+      select_reg_kernel<EW, kSelectThreads, kPosOut>                                                          \
+          <<<g, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, plan);          \
+  } while (0)
     if (e <= 8) QSA_SELECT_REG(8);
     else if (e <= 10) QSA_SELECT_REG(10);
     else if (e <= 12) QSA_SELECT_REG(12);
@@ -833,8 +923,12 @@ static void launch_select_t(const Meta& m, const float* scores, int64_t ld, int 
     return;
   }
   if (m.max_blocks <= kLongRowBlocks) {
-    select_reg_kernel<kLongRowBlocks / kSelectThreads, kSelectThreads, kPosOut>
-        <<<m.num_q, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width);
+    if (plan.words)
+      select_reg_kernel<kLongRowBlocks / kSelectThreads, kSelectThreads, kPosOut, true>
+          <<<nwg, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, plan);
+    else
+      select_reg_kernel<kLongRowBlocks / kSelectThreads, kSelectThreads, kPosOut>
+          <<<nwg, kSelectThreads, 0, stream>>>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, plan);
     return;
   }
   // Longer rows: every slice keeps its top k, then one workgroup per query
@@ -852,8 +946,15 @@ static void launch_select_t(const Meta& m, const float* scores, int64_t ld, int 
   else select_slice_kernel<16><<<sgrid, kSelectThreads, 0, stream>>>(m, scores, ld, k, lr);
   // the candidate step: 8 candidates per thread while they fit, on 512
   // threads for the few candidates of up to 8 slices
-#define QSA_SELECT_CAND(EW, NTW) \
-  select_cand_kernel<EW, NTW, kPosOut><<<m.num_q, NTW, 0, stream>>>(m, k, sel, n_sel, pos, n_pos, width, lr)
+#define QSA_SELECT_CAND(EW, NTW)                                                                        \
+  do {                                                                                                 \
+    if (plan.words)                                                                                    \
+      select_cand_kernel<EW, NTW, kPosOut, true><<<nwg, NTW, 0, stream>>>(m, k, sel, n_sel, pos, n_pos, width, \
+                                                                          lr, plan);                   \
+    else                                                                                               \
+      select_cand_kernel<EW, NTW, kPosOut><<<nwg, NTW, 0, stream>>>(m, k, sel, n_sel, pos, n_pos, width, lr, \
+                                                                    plan);                             \
+  } while (0)
   if (lr.cstride <= 8 * 512) QSA_SELECT_CAND(8, 512);
   else if (lr.cstride <= 8 * kSelectThreads) QSA_SELECT_CAND(8, kSelectThreads);
   else if (lr.cstride <= 16 * kSelectThreads) QSA_SELECT_CAND(16, kSelectThreads);
@@ -869,14 +970,20 @@ size_t select_workspace_bytes(int num_q, int max_blocks) {
 }
 
 hipError_t launch_select(const Meta& m, const float* scores, int64_t ld, int k, int32_t* sel, int32_t* n_sel,
-                         int32_t* pos, int32_t* n_pos, int width, bool run_heads, void* ws, hipStream_t stream) {
+                         int32_t* pos, int32_t* n_pos, int width, bool run_heads, void* ws, const AttnPlan& plan,
+                         hipStream_t stream) {
   uint32_t* ms_ws = static_cast<uint32_t*>(ws);
   if (pos && run_heads)
-    launch_select_t<kPosHeads>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, ms_ws, stream);
+    launch_select_t<kPosHeads>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, ms_ws, plan, stream);
   else if (pos)
-    launch_select_t<kPosFull>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, ms_ws, stream);
+    launch_select_t<kPosFull>(m, scores, ld, k, sel, n_sel, pos, n_pos, width, ms_ws, plan, stream);
   else
-    launch_select_t<kPosNone>(m, scores, ld, k, sel, n_sel, nullptr, nullptr, width, ms_ws, stream);
+    launch_select_t<kPosNone>(m, scores, ld, k, sel, n_sel, nullptr, nullptr, width, ms_ws, plan, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_plan(const Meta& m, const AttnPlan& plan, hipStream_t stream) {
+  attn_plan_kernel<<<1, 512, 0, stream>>>(m, plan);
   return hipGetLastError();
 }
 
