@@ -132,7 +132,8 @@ qsa_status qsa_error_read(uint32_t* bits, int clear);
  * 256-byte aligned and ZERO-FILLED before its first use.  It starts with a
  * control region of fixed size (128 KiB) that holds every counter any call
  * uses, at offsets that do not depend on the batch; the rest (scores,
- * selections, split partials, candidates) needs no initial contents.  Every
+ * selections, the attention's work list for batches of several requests,
+ * split partials, candidates) needs no initial contents.  Every
  * call leaves the counters it used at zero again, so one zero fill serves any
  * number of calls, of any batch geometry, on the same stream, provided each
  * call is given at least the bytes this function returns for its own batch
@@ -207,8 +208,11 @@ qsa_status qsa_build_index(const qsa_batch* batch, const int32_t* sel, const int
  * block): for every i < n_pos[q],  pos[q][i] = pos[q][i - i % 4] + i % 4.
  * The runs may come in any order; entries past n_pos[q] are not read.  A
  * buffer that breaks the run rule gives undefined output in release builds
- * and sets QSA_DEBUG_BAD_POSITIONS in a debug build (qsa_debug_error below).
- * Hq % Hkv == 0 and Hq / Hkv <= 16.  ws: qsa_workspace_bytes() for this k. */
+ * and sets QSA_ERROR_BAD_POSITIONS in a debug build (qsa_error_read above).
+ * Hq % Hkv == 0 and Hq / Hkv <= 16.  ws: qsa_workspace_bytes() for this k.
+ * A batch of several requests with fewer than 512 (query, KV head) units
+ * takes two launches: one workgroup lays out a longest-first work list from
+ * n_pos in the workspace, then the attention splits the units by it. */
 qsa_status qsa_sparse_attn(const qsa_batch* batch, const void* q, const void* k_cache,
                            const void* v_cache, int32_t kv_dtype, const float* k_scale,
                            const float* v_scale, int32_t num_q_heads, int32_t num_kv_heads,
