@@ -215,9 +215,11 @@ CSRC = os.path.join(ROOT, "block_sparse_attention_qsa_amd", "csrc")
 
 
 def _code_text(src: bytes) -> bytes:
-    """Source text without // comments, trailing blanks and empty lines: edits
-    to comments leave the hash (and the counters tied to it) valid."""
+    """Source text without /* */ and // comments, trailing blanks and empty
+    lines: edits to comments leave the hash (and the counters tied to it)
+    valid."""
     import re
+    src = re.sub(rb"/\*.*?\*/", b"", src, flags=re.S)
     lines = (re.sub(rb"//.*$", b"", l).rstrip() for l in src.splitlines())
     return b"\n".join(l for l in lines if l)
 
