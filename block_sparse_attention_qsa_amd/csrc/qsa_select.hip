@@ -785,14 +785,21 @@ __device__ __forceinline__ void build_attn_plan(const Meta& m, const AttnPlan& p
   const uint32_t fbefore = block_exclusive_scan<NT>((uint32_t)f, scan_s, &nfull);
   if (part) atomicAdd(&hist_s[rest], 1u);
   __syncthreads();
-  if (tid == 0) {
-    uint32_t run = 0u;
-    for (int c = kMaxSplitChunks; c >= 0; --c) {   // longest rest first
-      base_s[c] = run;
-      run += hist_s[c];
+  if (tid < kWave) {
+    // running totals of the rests, longest first: lane l takes the sizes
+    // kMaxSplitChunks - 2l and - 2l - 1
+    static_assert(2 * kWave > kMaxSplitChunks, "two sizes per lane");
+    const int i0 = 2 * tid, i1 = 2 * tid + 1;
+    const uint32_t h0 = i0 <= kMaxSplitChunks ? hist_s[kMaxSplitChunks - i0] : 0u;
+    const uint32_t h1 = i1 <= kMaxSplitChunks ? hist_s[kMaxSplitChunks - i1] : 0u;
+    const uint32_t inc = wave_inclusive_scan(h0 + h1);
+    const uint32_t before = inc - h0 - h1;
+    if (i0 <= kMaxSplitChunks) base_s[kMaxSplitChunks - i0] = before;
+    if (i1 <= kMaxSplitChunks) base_s[kMaxSplitChunks - i1] = before + h0;
+    if (tid == kWave - 1) {
+      pl.words[0] = (int32_t)((nfull + inc) * (uint32_t)H);
+      pl.words[1] = cps;
     }
-    pl.words[0] = (int32_t)((nfull + run) * (uint32_t)H);
-    pl.words[1] = cps;
   }
   __syncthreads();
   uint32_t* items = reinterpret_cast<uint32_t*>(pl.words + kPlanHeader);
