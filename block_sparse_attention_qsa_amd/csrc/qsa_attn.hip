@@ -6,8 +6,11 @@
 // contract.
 //
 // Work unit: (query, KV head, split of the position buffer), the position in
-// a 3-D grid dispatched query fastest and split slowest.  A wave takes 32
-// gathered positions per step and serves the whole GQA group of that KV head
+// a 3-D grid dispatched query fastest and split slowest - or, for a batch of
+// several requests with fewer than 512 units, item w of a longest-first work
+// list (AttnPlan) in a 1-D grid, the splits sized from the batch's total
+// positions so that long units get more workgroups than short ones.  A wave
+// takes 32 gathered positions per step and serves the whole GQA group of that KV head
 // (up to 16 query heads) at once on bf16 MFMA 16x16x32:
 //   S^T[pos][head] = K[pos][:] . Q[head][:]      (2 tiles x 4 MFMAs)
 //   O^T[dim][head] += V^T[dim][pos] P^T[pos][head]  (8 MFMAs each for the BF16

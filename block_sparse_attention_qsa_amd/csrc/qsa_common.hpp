@@ -162,7 +162,7 @@ constexpr int kLongRowBlocks = 32768;
 struct AttnSplit {
   int splits;            // workgroups per (query, KV head): the grid's third dimension
   int chunks_per_split;  // 32-position chunks per workgroup (multiple of kAttnWaves); with
-                         // ragged, the least the kernel takes
+                         // ragged, the least the work list takes
 };
 
 // ragged = false: every unit is split alike, into enough workgroups that
@@ -195,8 +195,9 @@ __host__ __device__ inline AttnSplit attn_split(int num_q, int num_kv_heads, int
 // its 65 chunks rounded up to whole 4-chunk steps.
 constexpr int kMaxSplitChunks = ((QSA_WIDTH + kChunk - 1) / kChunk + kAttnWaves - 1) / kAttnWaves * kAttnWaves;
 
-// Work list of the attention for a ragged batch inside qsa_decode, written
-// by one extra workgroup of the selection launch: kPlanHeader header words
+// Work list of the attention for a ragged batch, written by one extra
+// workgroup of the selection launch inside qsa_decode (or by a launch of its
+// own before qsa_sparse_attn): kPlanHeader header words
 // ([0] items, [1] chunks per split), then one word per item (query, KV
 // head, split, the unit's splits): every split of the full chunk count
 // first, then each unit's last, shorter split, longest first (a longest-
