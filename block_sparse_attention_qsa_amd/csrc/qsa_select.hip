@@ -31,7 +31,7 @@ constexpr int kHotLanes = 8;     // first scores of a wave in the top bin that m
 
 // Inside the fully unrolled per-element loops: a scheduling fence every 4
 // elements, so the compiler does not compute all E derived values before
-// consuming them (with 64 keys per thread in registers that spills).
+// consuming them (with 32 keys per thread in registers that would spill).
 __device__ __forceinline__ void sched_fence(int e) {
   if ((e & 3) == 3) __builtin_amdgcn_sched_barrier(0);
 }
@@ -149,8 +149,7 @@ __device__ __forceinline__ float wave_min_f32(float v) {
 
 // Register-resident selector for rows of at most E * NT blocks, NT threads
 // per query.  Thread t owns the contiguous segment [t*E, t*E + E): its
-// scores stay in registers (the upper half of a 64-wide segment in LDS) from
-// the load to the end.
+// scores stay in registers from the load to the end.
 //   1. One block reduction gives the row's smallest and largest score.  When
 //      both are finite and differ, one histogram pass bins the scores on a
 //      linear grid of 2,048 bins spanning [min, max] (grid_bin1 is monotone,
@@ -310,15 +309,8 @@ template <int E, int NT, bool kScores>
 __device__ __forceinline__ int select_core(const float (&sv)[E], const int nf, const int k, int32_t* sel_s,
                                            float* score_s) {
   constexpr int NW = NT / kWave;
-  constexpr int ER = E > 32 ? 32 : E;    // scores per thread held in registers
-  constexpr int EL = E - ER;             // the rest sit in LDS, column-major
   constexpr int kMapWords = E * NT / 32;
-  static_assert((E % 2 == 0 && E >= 8 && E <= 32) || E == 64, "segment widths");
-  // candidates are staged during classification, except for 64-wide segments
-  // whose register budget leaves no room for it (they stage in a loop of
-  // their own)
-  constexpr bool kFuseStage = E <= 32;
-  __shared__ float slab[EL > 0 ? EL * NT : 1];
+  static_assert(E % 2 == 0 && E >= 8 && E <= 32, "segment widths");
   // two histograms behind one guard word: the grid pass adds at hist_g[bin + 1]
   // and a NaN score (bin + 1 = 0) in a full wave lands in the guard, unread
   // (the grid total then misses it and the row takes the radix passes)
@@ -356,15 +348,11 @@ __device__ __forceinline__ int select_core(const float (&sv)[E], const int nf, c
 
   // Slots past the row become NaN: the range reduction skips them and their
   // grid bin is -1.
-  float xr[ER];
+  float xr[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const float x = e < cnt ? sv[e] : __builtin_nanf("");
-    if (e < ER) xr[e < ER ? e : 0] = x;
-    else slab[(e - ER) * NT + tid] = x;   // read back only by this thread
-  }
+  for (int e = 0; e < E; ++e) xr[e] = e < cnt ? sv[e] : __builtin_nanf("");
 // score e of this thread's segment (e is a compile-time constant in the unrolled loops)
-#define QSA_X(e) ((e) < ER ? xr[(e) < ER ? (e) : 0] : slab[((e) - ER) * NT + tid])
+#define QSA_X(e) xr[e]
 
   // ---- 1. score range of the row (NaN skipped)
   float vmax = -__builtin_inff(), vmin = __builtin_inff();
@@ -393,11 +381,9 @@ __device__ __forceinline__ int select_core(const float (&sv)[E], const int nf, c
   // ---- 2. grid histogram, then classification
   int B0 = 0, h = 0;
   uint32_t krem = (uint32_t)k, c0 = (uint32_t)nf;
-  // Segments of up to 32 elements keep each element's grid bin from the
-  // histogram pass (bin + 1, 0 for none; two per word), so classifying needs
-  // no second bin computation.
-  constexpr bool kKeepBins = E <= 32;
-  uint32_t bins[kKeepBins ? E / 2 : 1];
+  // Each element's grid bin from the histogram pass is kept (bin + 1, 0 for
+  // none; two per word), so classifying needs no second bin computation.
+  uint32_t bins[E / 2];
   if (grid) {
     const float c0f = fresh_uniform(cgrid), inv0 = fresh_uniform(inv);
     // A wave whose first scores land in the grid's top bin several times
@@ -415,10 +401,8 @@ __device__ __forceinline__ int select_core(const float (&sv)[E], const int nf, c
     const bool top = (HOT) && b1 == kRadixBins;                 \
     if (HOT) ntop += top ? 1u : 0u;                             \
     if (((FULL) || b1 > 0) && !top) atomicAdd(&hist_g[b1], 1u); \
-    if (kKeepBins) {                                            \
-      if (e & 1) bins[e >> 1] |= (uint32_t)b1 << 16;            \
-      else bins[e >> 1] = (uint32_t)b1;                         \
-    }                                                           \
+    if (e & 1) bins[e >> 1] |= (uint32_t)b1 << 16;              \
+    else bins[e >> 1] = (uint32_t)b1;                           \
     sched_fence(e);                                             \
   }
     if (wave_full) {
@@ -458,25 +442,14 @@ __device__ __forceinline__ int select_core(const float (&sv)[E], const int nf, c
   inb.clear();
   if (grid) {
     if (!wave_empty) {
-      if (kKeepBins) {
-        const uint32_t b1 = (uint32_t)B0 + 1u;
+      const uint32_t b1 = (uint32_t)B0 + 1u;
 #pragma unroll
-        for (int e = E - 1; e >= 0; --e) {
-          const uint32_t b = (bins[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-          above.push(e, b > b1);
-          inb.push(e, b == b1);
-        }
-      } else {
-        const float c1f = fresh_uniform(cgrid), inv1 = fresh_uniform(inv);
-#pragma unroll
-        for (int e = E - 1; e >= 0; --e) {
-          const int b1 = grid_bin1(QSA_X(e), c1f, inv1);
-          above.push(e, b1 > B0 + 1);
-          inb.push(e, b1 == B0 + 1);
-          sched_fence(e);
-        }
+      for (int e = E - 1; e >= 0; --e) {
+        const uint32_t b = (bins[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        above.push(e, b > b1);
+        inb.push(e, b == b1);
       }
-      if (kFuseStage && ranked) {
+      if (ranked) {
         // Stage this thread's candidates (few in a row, so most waves skip
         // this): one LDS append per thread that has any.
         const uint32_t mine = inb.count();
@@ -505,22 +478,6 @@ __device__ __forceinline__ int select_core(const float (&sv)[E], const int nf, c
 #pragma unroll
     for (int i = 0; i < ElemBits<E>::W; ++i) keep.w[i] |= inb.w[i];   // B0 kept whole
   } else if (ranked) {
-    if (!kFuseStage) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const bool mine = inb.test(e);
-        const uint64_t bal = __ballot(mine);
-        if (bal) {
-          uint32_t wbase = 0;
-          if (lane == __builtin_ctzll(bal)) wbase = atomicAdd(&s_ncand, (uint32_t)__popcll(bal));
-          wbase = (uint32_t)__builtin_amdgcn_readlane((int)wbase, __builtin_ctzll(bal));
-          const uint32_t slot =
-              __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-          if (mine && wbase + slot < (uint32_t)kCandCap)
-            cand_s[wbase + slot] = u32x2{score_key(QSA_X(e)), (uint32_t)(beg + e)};
-        }
-      }
-    }
     __syncthreads();
     if (tid < (int)c0) {
       const u32x2 me = cand_s[tid];
@@ -532,10 +489,7 @@ __device__ __forceinline__ int select_core(const float (&sv)[E], const int nf, c
       if (ahead < krem) atomicOr(&keepmap[me.y >> 5], 1u << (me.y & 31));
     }
     __syncthreads();
-    if (E == 64) {
-      keep.w[0] |= keepmap[2 * tid];
-      keep.w[ElemBits<E>::W - 1] |= keepmap[2 * tid + 1];
-    } else {
+    {
       // this thread's E bits start at bit tid*E and may run into the next word
       const int bit0 = tid * E, sh = bit0 & 31;
       uint32_t word = keepmap[bit0 >> 5] >> sh;
