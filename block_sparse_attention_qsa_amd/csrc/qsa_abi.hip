@@ -351,8 +351,10 @@ qsa_status qsa_sparse_attn(const qsa_batch* batch, const void* q, const void* k_
     return QSA_ERR_SHAPE;
   const int k = (width - (QSA_BLOCK - 1)) / QSA_BLOCK;
   const WsLayout w = ws_layout(batch->num_q, batch->max_blocks, num_q_heads, num_kv_heads, k);
-  // unsplit attention (units alone fill the chip) touches no workspace
-  QSA_TRY(check_ws(ws, ws_bytes, w.attn_end > w.partials ? w.attn_end : 0));
+  // A ragged batch writes its work list there even when no unit is split;
+  // otherwise only split units (partials and arrival counters) use it.
+  const bool ragged = qsa::attn_ragged(batch->num_req, batch->num_q, num_kv_heads);
+  QSA_TRY(check_ws(ws, ws_bytes, ragged || w.attn_end > w.partials ? w.attn_end : 0));
   char* base = static_cast<char*>(ws);
   qsa::AttnArgs a;
   a.q = q;
@@ -375,7 +377,7 @@ qsa_status qsa_sparse_attn(const qsa_batch* batch, const void* q, const void* k_
   a.plan = nullptr;
   a.err = device_error_word();
   const qsa::Meta m = meta_of(batch);
-  if (qsa::attn_ragged(m.num_req, m.num_q, num_kv_heads)) {
+  if (ragged) {
     // a ragged batch: a work list from the given position counts first
     qsa::AttnPlan plan{reinterpret_cast<int32_t*>(base + w.plan), num_kv_heads, k,
                        qsa::attn_split(m.num_q, num_kv_heads, width, true).chunks_per_split, n_pos, width};

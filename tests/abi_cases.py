@@ -102,6 +102,13 @@ def check_error_paths(lib, CBatch):
     assert args(32, 4, 0, None, 2051, 0.08, 0, None, 0) == 4                 # workspace needed (split units)
     assert args(32, 4, 0, None, 2051, 0.08, 0, ctypes.c_void_p(0x1004), 1 << 30) == 4   # misaligned
     assert args(32, 4, 0, None, 2051, 0.08, 0, P, 4096) == 4                 # too small
+    # a batch of several requests writes the attention's work list to the
+    # workspace even when no unit is split (k = 1: one 32-position chunk)
+    two = cbatch(CBatch, num_req=2, num_q=4, max_blocks=8)
+    rag = lambda ws, wsn: lib.qsa_sparse_attn(ctypes.byref(two), P, P, P, 0, None, None, 32, 4, P, P, 7, 0.08, P, 0,
+                                              ws, wsn, None)
+    assert rag(None, 0) == 4
+    assert rag(P, 128 * 1024) == 4
     # output alignment: 16 bytes for FP32, 8 for BF16
     att_out = lambda out, odt: lib.qsa_sparse_attn(ctypes.byref(good), P, P, P, 0, None, None, 32, 4, P, P, 2051,
                                                    0.08, out, odt, P, 1 << 30, None)

@@ -314,6 +314,34 @@ def test_build_index_bit_exact():
     assert np.array_equal(n_pos.cpu().numpy(), ref["n_pos"])
 
 
+@pytest.mark.parametrize("k", [1, 7, 31])
+def test_sparse_attn_small_k_several_requests(k):
+    """Position rows of 4k + 3 <= 127 entries (one 32-position chunk step, so
+    no unit is split) on a batch of several requests: the attention still
+    follows the work list it lays out in the workspace, and the call without a
+    workspace is refused before anything is enqueued."""
+    need_gpu()
+    w = _mixed_workload(kv="fp8_e4m3", hq=32, hkv=4, seed=207)
+    say("qsa_sparse_attn small k", k, w.name)
+    ref = oracle_decode(w, want_scores=False, k=k)
+    dev = upload(w)
+    b = batch_of(w)
+    pos = torch.from_numpy(ref["pos"]).cuda()
+    n_pos = torch.from_numpy(ref["n_pos"]).cuda()
+    assert pos.shape[1] == 4 * k + 3
+    out = torch.full((w.num_q, w.num_q_heads, 128), float("nan"), dtype=torch.float32, device="cuda")
+    with pytest.raises(qsa.QsaError):
+        qsa.qsa_sparse_attn(b, dev["q"], dev["k_cache"], dev["v_cache"], pos, n_pos, out, k_scale=dev["k_scale"],
+                            v_scale=dev["v_scale"], sm_scale=SM_SCALE)
+    ws = qsa.alloc_workspace(b, w.num_q_heads, w.num_kv_heads, k)
+    for rep in range(2):
+        qsa.qsa_sparse_attn(b, dev["q"], dev["k_cache"], dev["v_cache"], pos, n_pos, out, k_scale=dev["k_scale"],
+                            v_scale=dev["v_scale"], sm_scale=SM_SCALE, workspace=ws)
+        torch.cuda.synchronize()
+        assert_out_close(out.cpu().numpy().astype(np.float64), ref["out"])
+        assert int(ws[:128 * 1024].sum().item()) == 0
+
+
 @pytest.mark.parametrize("kv,hq,hkv,out_dtype", [
     ("bf16", 16, 2, "f32"), ("fp8_e4m3", 16, 2, "f32"), ("bf16", 32, 4, "bf16"), ("fp8_e4m3", 32, 4, "bf16"),
     ("bf16", 4, 4, "f32"), ("bf16", 8, 2, "f32"), ("fp8_e4m3", 32, 2, "f32"), ("bf16", 12, 3, "f32"),
