@@ -126,7 +126,7 @@ class Rig:
         else:
             raise KeyError(name)
 
-    def timed_graph(self, fn, steps: int, warmup: int, reps: int = 3, flush: bool = False):
+    def timed_graph(self, fn, steps: int, warmup: int, reps: int = 5, flush: bool = False):
         """Capture `steps` calls of fn(i) in a HIP graph; return (median ms per
         call over reps replays, wall-clock ms per call of the last replay).
         With flush, every timed replay is preceded (outside the timed region)
