@@ -11,6 +11,7 @@ import torch
 
 import block_sparse_attention_qsa_amd as qsa
 import oracle
+from workloads import paged_layout
 from workloads.device import upload
 
 SM_SCALE = 1.0 / math.sqrt(128)
@@ -95,3 +96,47 @@ def assert_out_close(gpu_out, ref_out, queries=None, tol=OUT_TOL):
     assert cfg <= tol, cfg
     assert per_q <= tol, per_q
     return cfg, per_q
+
+
+def bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def decode_paged(w, page_size, seed, dev=None, k=qsa.TOPK):
+    """qsa_decode of workload w through a paged copy of its KV cache (pages of
+    page_size tokens scattered by a seeded permutation); also checks that the
+    production call and the stage path (qsa_build_index on the selection)
+    agree with it bit for bit.  Returns (results, page table, K, V pages)."""
+    table, kc, vc = paged_layout(w, page_size, seed)
+    d = upload(w) if dev is None else dict(dev)
+    if w.kv_dtype == "bf16":
+        d["k_cache"], d["v_cache"] = bf16_dev(kc), bf16_dev(vc)
+    else:
+        d["k_cache"] = torch.from_numpy(np.ascontiguousarray(kc)).cuda().view(torch.float8_e4m3fn)
+        d["v_cache"] = torch.from_numpy(np.ascontiguousarray(vc)).cuda().view(torch.float8_e4m3fn)
+    b = qsa.Batch(w.q_start, w.seq_len, None, w.blk_start, page_table=table, page_size=page_size)
+    hq = w.num_q_heads
+    out = torch.full((w.num_q, hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    sel = torch.full((w.num_q, k), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.full((w.num_q,), -7, dtype=torch.int32, device="cuda")
+    pos = torch.full((w.num_q, 4 * k + 3), -7, dtype=torch.int32, device="cuda")
+    n_pos = torch.full((w.num_q,), -7, dtype=torch.int32, device="cuda")
+    ws = qsa.alloc_workspace(b, hq, w.num_kv_heads, k)
+    qsa.qsa_decode(b, d["idx_q"], d["ckeys"], d["q"], d["k_cache"], d["v_cache"], out, ws, k_scale=d["k_scale"],
+                   v_scale=d["v_scale"], k=k, sm_scale=SM_SCALE, sel=sel, n_sel=n_sel, pos=pos, n_pos=n_pos)
+    # the production call (no sel / n_sel / pos requested)
+    out_lean = torch.full_like(out, float("nan"))
+    n_pos_lean = torch.full_like(n_pos, -7)
+    qsa.qsa_decode(b, d["idx_q"], d["ckeys"], d["q"], d["k_cache"], d["v_cache"], out_lean, ws,
+                   k_scale=d["k_scale"], v_scale=d["v_scale"], k=k, sm_scale=SM_SCALE, n_pos=n_pos_lean)
+    # the stage path: selection without positions, then the index builder
+    pos2 = torch.full_like(pos, -7)
+    n_pos2 = torch.full_like(n_pos, -7)
+    qsa.qsa_build_index(b, sel, n_sel, pos2, n_pos2, k=k)
+    torch.cuda.synchronize()
+    res = {"out": out.cpu().numpy().astype(np.float64), "sel": sel.cpu().numpy(), "n_sel": n_sel.cpu().numpy(),
+           "pos": pos.cpu().numpy(), "n_pos": n_pos.cpu().numpy()}
+    assert np.array_equal(pos2.cpu().numpy(), res["pos"]) and np.array_equal(n_pos2.cpu().numpy(), res["n_pos"])
+    assert np.array_equal(n_pos_lean.cpu().numpy(), res["n_pos"])
+    assert np.array_equal(out_lean.cpu().numpy().view(np.uint32), out.cpu().numpy().view(np.uint32))
+    return res, table, kc, vc

@@ -8,15 +8,12 @@ import torch
 
 import block_sparse_attention_qsa_amd as qsa
 import oracle
-from workloads import bf16_bits_from_f32, make_custom, paged_layout
+from workloads import bf16_bits_from_f32, make_custom
 from workloads.device import upload
-from gpu_helpers import SM_SCALE, assert_out_close, assert_selection_equal, need_gpu, run_decode, say
+from gpu_helpers import (SM_SCALE, assert_out_close, assert_selection_equal, bf16_dev, decode_paged, need_gpu,
+                         run_decode, say)
 
 pytestmark = pytest.mark.gpu
-
-
-def _bf16_dev(bits):
-    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
 
 
 def _bits(t):
@@ -59,11 +56,11 @@ def test_compress_keys(paged):
     tok = _token_keys(rng, slots)
     nrows = int(blk_start[-1] + rows[-1] + 8)
     ck_init = np.full((nrows, 128), 0x7E7E, np.uint16)
-    ck = _bf16_dev(ck_init)
+    ck = bf16_dev(ck_init)
     b = qsa.Batch(np.arange(nreq + 1), seq, None if paged else kv_start, blk_start,
                   page_table=table, page_size=page_size if paged else None)
     say("qsa_compress_keys paged" if paged else "qsa_compress_keys", nreq, "requests")
-    qsa.qsa_compress_keys(b, torch.from_numpy(prev.astype(np.int32)).cuda(), _bf16_dev(tok), ck)
+    qsa.qsa_compress_keys(b, torch.from_numpy(prev.astype(np.int32)).cuda(), bf16_dev(tok), ck)
     torch.cuda.synchronize()
     got = _bits(ck)
     want = ck_init.copy()
@@ -75,48 +72,12 @@ def test_compress_keys(paged):
     assert np.array_equal(got, want)
 
 
-def _decode_paged(w, page_size, seed, dev=None):
-    table, kc, vc = paged_layout(w, page_size, seed)
-    d = upload(w) if dev is None else dict(dev)
-    if w.kv_dtype == "bf16":
-        d["k_cache"], d["v_cache"] = _bf16_dev(kc), _bf16_dev(vc)
-    else:
-        d["k_cache"] = torch.from_numpy(np.ascontiguousarray(kc)).cuda().view(torch.float8_e4m3fn)
-        d["v_cache"] = torch.from_numpy(np.ascontiguousarray(vc)).cuda().view(torch.float8_e4m3fn)
-    b = qsa.Batch(w.q_start, w.seq_len, None, w.blk_start, page_table=table, page_size=page_size)
-    k, hq = qsa.TOPK, w.num_q_heads
-    out = torch.full((w.num_q, hq, 128), float("nan"), dtype=torch.float32, device="cuda")
-    sel = torch.full((w.num_q, k), -7, dtype=torch.int32, device="cuda")
-    n_sel = torch.full((w.num_q,), -7, dtype=torch.int32, device="cuda")
-    pos = torch.full((w.num_q, 4 * k + 3), -7, dtype=torch.int32, device="cuda")
-    n_pos = torch.full((w.num_q,), -7, dtype=torch.int32, device="cuda")
-    ws = qsa.alloc_workspace(b, hq, w.num_kv_heads, k)
-    qsa.qsa_decode(b, d["idx_q"], d["ckeys"], d["q"], d["k_cache"], d["v_cache"], out, ws, k_scale=d["k_scale"],
-                   v_scale=d["v_scale"], sm_scale=SM_SCALE, sel=sel, n_sel=n_sel, pos=pos, n_pos=n_pos)
-    # the production call (no sel / n_sel / pos requested)
-    out_lean = torch.full_like(out, float("nan"))
-    n_pos_lean = torch.full_like(n_pos, -7)
-    qsa.qsa_decode(b, d["idx_q"], d["ckeys"], d["q"], d["k_cache"], d["v_cache"], out_lean, ws,
-                   k_scale=d["k_scale"], v_scale=d["v_scale"], sm_scale=SM_SCALE, n_pos=n_pos_lean)
-    # the stage path: selection without positions, then the index builder
-    pos2 = torch.full_like(pos, -7)
-    n_pos2 = torch.full_like(n_pos, -7)
-    qsa.qsa_build_index(b, sel, n_sel, pos2, n_pos2)
-    torch.cuda.synchronize()
-    res = {"out": out.cpu().numpy().astype(np.float64), "sel": sel.cpu().numpy(), "n_sel": n_sel.cpu().numpy(),
-           "pos": pos.cpu().numpy(), "n_pos": n_pos.cpu().numpy()}
-    assert np.array_equal(pos2.cpu().numpy(), res["pos"]) and np.array_equal(n_pos2.cpu().numpy(), res["n_pos"])
-    assert np.array_equal(n_pos_lean.cpu().numpy(), res["n_pos"])
-    assert np.array_equal(out_lean.cpu().numpy().view(np.uint32), out.cpu().numpy().view(np.uint32))
-    return res, table, kc, vc
-
-
 @pytest.mark.parametrize("kv,page_size", [("bf16", 16), ("fp8_e4m3", 64), ("bf16", 4)])
 def test_paged_decode(kv, page_size):
     need_gpu()
     w = make_custom("paged", [9000, 3001, 57, 20003, 2052], [4, 2, 1, 4, 3], 32, 4, kv_dtype=kv, seed=710)
     say("paged qsa_decode", kv, "page size", page_size)
-    got, table, kc, vc = _decode_paged(w, page_size, 711)
+    got, table, kc, vc = decode_paged(w, page_size, 711)
     ref = oracle.decode(w.q_start, w.seq_len, w.kv_start, w.blk_start, w.idx_q, w.ckeys, w.q, kc, vc,
                         w.kv_dtype, w.k_scale, w.v_scale, sm_scale=SM_SCALE, want_scores=False,
                         page_table=table, page_size=page_size)
@@ -128,19 +89,19 @@ def test_paged_decode(kv, page_size):
     assert np.array_equal(flat["out"].view(np.uint64), got["out"].view(np.uint64))
 
 
-
 def test_paged_decode_long_row():
     """Paged KV with a row past 32,768 blocks (140,000 tokens): the two-step
     long-row selection writes positions through the page table."""
     need_gpu()
     w = make_custom("paged-long", [140000, 57, 3001], [4, 1, 2], 16, 2, kv_dtype="fp8_e4m3", seed=712)
     say("paged qsa_decode, long row")
-    got, table, kc, vc = _decode_paged(w, 64, 713)
+    got, table, kc, vc = decode_paged(w, 64, 713)
     ref = oracle.decode(w.q_start, w.seq_len, w.kv_start, w.blk_start, w.idx_q, w.ckeys, w.q, kc, vc,
                         w.kv_dtype, w.k_scale, w.v_scale, sm_scale=SM_SCALE, want_scores=False,
                         page_table=table, page_size=64)
     assert_selection_equal(got, ref)
     assert_out_close(got["out"], ref["out"])
+
 
 def test_draft_steps_reuse_selection():
     """A verify step selects; later draft steps of each request (after 1..4

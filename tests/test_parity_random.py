@@ -14,8 +14,8 @@ import torch
 
 from workloads import make_custom
 from workloads.device import upload
-from gpu_helpers import (OUT_TOL, assert_lean_decode_same, assert_out_close, assert_selection_equal, need_gpu,
-                         oracle_decode, run_decode, say)
+from gpu_helpers import (OUT_TOL, SM_SCALE, assert_lean_decode_same, assert_out_close, assert_selection_equal,
+                         decode_paged, need_gpu, oracle_decode, run_decode, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,3 +69,21 @@ def test_random_decode(seed):
     else:
         assert_out_close(got["out"], ref["out"])
     assert_lean_decode_same(w, got, dev, k=k, out_dtype=out_dtype)
+
+
+@pytest.mark.parametrize("seed", list(range(16)))
+def test_random_decode_paged(seed):
+    """The same random batches through a paged KV cache: pages of 4 to 256
+    tokens scattered over the cache by a seeded permutation."""
+    import oracle
+    need_gpu()
+    lens, nq, hkv, group, kv, k, _, iv = _case(3000 + seed)
+    page_size = int(np.random.default_rng(4000 + seed).choice([4, 8, 16, 64, 256]))
+    say(f"paged case {seed}: lens {lens} nq {nq} Hkv {hkv} G {group} {kv} k {k} {iv} page {page_size}")
+    w = make_custom(f"randp{seed}", lens, nq, group * hkv, hkv, kv_dtype=kv, seed=5000 + seed, index_values=iv)
+    got, table, kc, vc = decode_paged(w, page_size, 6000 + seed, k=k)
+    ref = oracle.decode(w.q_start, w.seq_len, w.kv_start, w.blk_start, w.idx_q, w.ckeys, w.q, kc, vc, w.kv_dtype,
+                        w.k_scale, w.v_scale, k=k, sm_scale=SM_SCALE, want_scores=False, page_table=table,
+                        page_size=page_size)
+    assert_selection_equal(got, ref)
+    assert_out_close(got["out"], ref["out"])
