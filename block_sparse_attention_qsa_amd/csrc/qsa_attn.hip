@@ -432,10 +432,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnParams p) {
     cps = min(max(p.plan[1], 1), kMaxSplitChunks);
     const uint32_t e = (uint32_t)p.plan[kPlanHeader + w];   // the grid never exceeds the list's room
     if (w >= items) return;
-    q = (int)(e & 0xFFFu);
-    g = (int)((e >> 12) & 0x7Fu);
-    s = (int)((e >> 19) & 0x1Fu);
-    S = (int)((e >> 24) & 0x1Fu);
+    plan_unpack(e, q, g, s, S);
     q = min(q, p.num_q - 1);
     g = min(g, Hkv - 1);
     S = min(max(S, 1), p.splits);

@@ -204,8 +204,23 @@ constexpr int kMaxSplitChunks = ((QSA_WIDTH + kChunk - 1) / kChunk + kAttnWaves 
 // first list: the long work starts first, short work fills in at the end).
 // Attention workgroup w takes item w.
 constexpr int kPlanHeader = 16;
+// An item packs (query, KV head, split, splits) into 9 + 8 + 5 + 5 bits: a
+// list exists only while query x KV head units number under 512 on a batch
+// of two or more queries, so q < 256 and g < 256 whenever both are in use
+// (q < 512 alone), and a unit has at most kMaxSplits (17) splits.
+constexpr int kPlanQBits = 9, kPlanGBits = 8, kPlanSBits = 5;
+static_assert(kMaxSplits < (1 << kPlanSBits), "split index and count fit their fields");
+static_assert(kAttnTargetWgs <= (1 << kPlanQBits) && kAttnTargetWgs / 2 <= (1 << kPlanGBits),
+              "query and KV head indices of a listed batch fit their fields");
 __host__ __device__ inline uint32_t plan_item(int q, int g, int s, int S) {
-  return (uint32_t)q | ((uint32_t)g << 12) | ((uint32_t)s << 19) | ((uint32_t)S << 24);
+  return (uint32_t)q | ((uint32_t)g << kPlanQBits) | ((uint32_t)s << (kPlanQBits + kPlanGBits)) |
+         ((uint32_t)S << (kPlanQBits + kPlanGBits + kPlanSBits));
+}
+__host__ __device__ inline void plan_unpack(uint32_t e, int& q, int& g, int& s, int& S) {
+  q = (int)(e & ((1u << kPlanQBits) - 1u));
+  g = (int)((e >> kPlanQBits) & ((1u << kPlanGBits) - 1u));
+  s = (int)((e >> (kPlanQBits + kPlanGBits)) & ((1u << kPlanSBits) - 1u));
+  S = (int)((e >> (kPlanQBits + kPlanGBits + kPlanSBits)) & ((1u << kPlanSBits) - 1u));
 }
 struct AttnPlan {
   int32_t* words;         // header + items (workspace); nullptr: no plan

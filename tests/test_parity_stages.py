@@ -314,6 +314,31 @@ def test_build_index_bit_exact():
     assert np.array_equal(n_pos.cpu().numpy(), ref["n_pos"])
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_ragged_batch_many_kv_heads(kv):
+    """A batch of several requests whose (query, KV head) units stay under 512
+    with 136 KV heads (GQA group 1), so the attention's work list carries KV
+    head indices past 127: the fused decode (list written by the selection
+    launch) and the stage attention (list from n_pos) against the oracle."""
+    need_gpu()
+    w = make_custom(f"heads136-{kv}", [600, 2100, 3001], [1, 1, 1], 136, 136, kv_dtype=kv, seed=209)
+    say("ragged batch, 136 KV heads", kv)
+    ref = oracle_decode(w, want_scores=False)
+    dev = upload(w)
+    got = run_decode(w, dev)
+    assert_selection_equal(got, ref)
+    assert_out_close(got["out"], ref["out"])
+    assert_lean_decode_same(w, got, dev)
+    b = batch_of(w)
+    out = torch.full((w.num_q, w.num_q_heads, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ws = qsa.alloc_workspace(b, w.num_q_heads, w.num_kv_heads)
+    qsa.qsa_sparse_attn(b, dev["q"], dev["k_cache"], dev["v_cache"], torch.from_numpy(ref["pos"]).cuda(),
+                        torch.from_numpy(ref["n_pos"]).cuda(), out, k_scale=dev["k_scale"], v_scale=dev["v_scale"],
+                        sm_scale=SM_SCALE, workspace=ws)
+    torch.cuda.synchronize()
+    assert_out_close(out.cpu().numpy().astype(np.float64), ref["out"])
+
+
 @pytest.mark.parametrize("k", [1, 7, 31])
 def test_sparse_attn_small_k_several_requests(k):
     """Position rows of 4k + 3 <= 127 entries (one 32-position chunk step, so
