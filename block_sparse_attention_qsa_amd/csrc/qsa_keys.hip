@@ -5,9 +5,10 @@
 // groups tokens into 4-token micro-blocks and computes one compressed index
 // key per block; it does not state the compression.  The key used here is the
 // mean of the block's four per-token index keys, summed in FP64 in token order
-// and rounded once to BF16 (nearest, ties to even).  With BF16 inputs the FP64
-// sum is exact unless the four values span more than 2^45 in magnitude, so the
-// result is the correctly rounded mean.
+// and rounded once to BF16 (nearest, ties to even).  Four BF16 values whose
+// exponents differ by at most 43 need at most 53 significand bits in their
+// sum, so the FP64 sum is then exact and the result the correctly rounded
+// mean.
 //
 // One workgroup per request; each wave takes one new block at a time, lane l
 // owning dimensions 2l and 2l+1 (one 4-byte load per token, 256 B per wave).
