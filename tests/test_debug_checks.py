@@ -13,7 +13,7 @@ import torch
 import block_sparse_attention_qsa_amd as qsa
 from workloads import make_custom, paged_layout
 from workloads.device import upload
-from gpu_helpers import SM_SCALE, batch_of, need_gpu, run_decode, say
+from gpu_helpers import SM_SCALE, batch_of, decode_paged, need_gpu, run_decode, say
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +48,44 @@ def test_valid_inputs_report_nothing_and_match_release(debug_lib):
     qsa.use_library(True)
     assert np.array_equal(got["pos"], rel["pos"])
     assert np.array_equal(got["out"].view(np.uint64), rel["out"].view(np.uint64))
+
+
+def test_valid_paged_long_row_and_stage_calls_report_nothing(debug_lib):
+    """Valid inputs on the paths the first case does not take: a paged cache
+    with a row past 32,768 blocks (two-step selection, positions through the
+    page table; the stage index builder runs inside decode_paged too) and the
+    stage attention over positions in permuted runs.  The word stays 0 and the
+    bits equal the release library's."""
+    w = make_custom("dbg-valid-long", [140000, 57, 3001], [4, 1, 2], 16, 2, kv_dtype="fp8_e4m3", seed=1310)
+    say("debug build: valid paged long row")
+    got = decode_paged(w, 64, 1311)[0]
+    assert qsa.error_read(clear=True) == 0
+    dev = upload(w)
+    b = batch_of(w)
+    rng = np.random.default_rng(1312)
+    dbg = run_decode(w, dev)
+    pos = dbg["pos"].copy()
+    for qi in range(w.num_q):          # the kept blocks' 4-slot runs in another order
+        full = int(dbg["n_pos"][qi]) // 4
+        order = rng.permutation(full)
+        pos[qi, :4 * full] = pos[qi, :4 * full].reshape(full, 4)[order].reshape(-1)
+    outs = []
+    for debug in (True, False):
+        qsa.use_library(debug)
+        out = torch.full((w.num_q, 16, 128), float("nan"), dtype=torch.float32, device="cuda")
+        ws = qsa.alloc_workspace(b, 16, 2)
+        qsa.qsa_sparse_attn(b, dev["q"], dev["k_cache"], dev["v_cache"], torch.from_numpy(pos).cuda(),
+                            torch.from_numpy(dbg["n_pos"]).cuda(), out, k_scale=dev["k_scale"],
+                            v_scale=dev["v_scale"], sm_scale=SM_SCALE, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+        assert qsa.error_read(clear=True) == 0
+    qsa.use_library(False)
+    rel = decode_paged(w, 64, 1311)[0]
+    qsa.use_library(True)
+    assert np.array_equal(got["pos"], rel["pos"])
+    assert np.array_equal(got["out"].view(np.uint64), rel["out"].view(np.uint64))
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
 
 
 def test_page_past_the_table_row(debug_lib):
