@@ -122,9 +122,10 @@ int qsa_debug_build(void);
 
 /* Diagnostics: the OR of the QSA_ERROR_* bits kernels have set on the current
  * device since the word was last cleared, into *bits [host]; clear != 0 resets
- * it.  The word is the library's only state (one per device, zero when the
- * library is loaded).  Unlike every other call this one synchronises: it waits
- * for the device to finish its work and copies 4 bytes back. */
+ * it.  The word (one per device, zero when the library is loaded) is, with
+ * qsa_decode_static's scratch, all the state the library keeps.  Unlike every
+ * other call this one synchronises: it waits for the device to finish its work
+ * and copies 4 bytes back. */
 qsa_status qsa_error_read(uint32_t* bits, int clear);
 
 /* Bytes of device workspace qsa_select_topk / qsa_sparse_attn / qsa_decode need
@@ -237,9 +238,9 @@ qsa_status qsa_compress_keys(const qsa_batch* batch, const int32_t* prev_len, co
 /* a1..a4 in one call, the whole decode / MTP-verify step of one QSA layer for
  * the batch.  This is the stand-in for the chain the arex-research.com article
  * (four optimisations, item 4) overlaps with programmatic dependent launch on
- * its hardware ("QSA logits select plus attention", 1.249 us saved at batch
- * 1): here the stages are consecutive kernels on one stream with no host
- * involvement between them.  Scores, selection and positions live in the
+ * its hardware (selection and attention, 1.249 us saved at batch 1): here the
+ * stages are consecutive kernels on one stream with no host involvement
+ * between them.  Scores, selection and positions live in the
  * workspace, and
  * sel_opt [num_q][k] / n_sel_opt / pos_opt [num_q][4k+3] / n_pos_opt, when not
  * NULL, receive copies of the selection and position buffers for inspection.
