@@ -50,7 +50,7 @@ def _case(seed):
     return lens, nq, hkv, group, kv, k, out_bf16, iv
 
 
-@pytest.mark.parametrize("seed", list(range(40)))
+@pytest.mark.parametrize("seed", list(range(64)))
 def test_random_decode(seed):
     need_gpu()
     lens, nq, hkv, group, kv, k, out_bf16, iv = _case(1000 + seed)
@@ -71,7 +71,7 @@ def test_random_decode(seed):
     assert_lean_decode_same(w, got, dev, k=k, out_dtype=out_dtype)
 
 
-@pytest.mark.parametrize("seed", list(range(16)))
+@pytest.mark.parametrize("seed", list(range(32)))
 def test_random_decode_paged(seed):
     """The same random batches through a paged KV cache: pages of 4 to 256
     tokens scattered over the cache by a seeded permutation."""
