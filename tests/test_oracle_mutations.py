@@ -209,11 +209,80 @@ def _m_compress_first_block_off(m):
     m.compress_new_keys = compress_new_keys
 
 
+def _m_v_from_k(m):
+    orig = m.sparse_attention
+    m.sparse_attention = lambda qh, kr, vr, sm: orig(qh, kr, kr, sm)
+
+
+def _m_softmax_unnormalised(m):
+    def sparse_attention(q_heads, k_rows, v_rows, sm_scale):
+        Hq, d = q_heads.shape
+        G = Hq // k_rows.shape[1]
+        out = np.empty((Hq, d))
+        for h in range(Hq):
+            z = (k_rows[:, h // G, :] @ q_heads[h]) * sm_scale
+            out[h] = np.exp(z - z.max()) @ v_rows[:, h // G, :]
+        return out
+    m.sparse_attention = sparse_attention
+
+
+def _m_block_index_not_scaled(m):
+    def build_positions(sel, L, kv_start, k=m.TOPK, page_row=None, page_size=None):
+        sel = np.asarray(sel, dtype=np.int64)
+        nf = L // m.BLOCK
+        sel = sel[sel < nf]
+        full = (sel[:, None] + np.arange(m.BLOCK)[None, :]).reshape(-1)
+        p = m.token_slots(np.concatenate([full, np.arange(m.BLOCK * nf, L)]), kv_start, page_row, page_size)
+        out = np.full(m.BLOCK * k + m.BLOCK - 1, -1, dtype=np.int64)
+        out[:p.shape[0]] = p
+        return out, int(p.shape[0])
+    m.build_positions = build_positions
+
+
+def _m_partial_block_from_block_start(m):
+    orig = m.build_positions
+    def build_positions(sel, L, kv_start, k=m.TOPK, page_row=None, page_size=None):
+        out, n = orig(sel, L, kv_start, k, page_row, page_size)
+        pl = L % m.BLOCK
+        if pl:
+            nf = L // m.BLOCK
+            out = out.copy()
+            out[n - pl:n] = m.token_slots(np.arange(m.BLOCK * (nf - 1), m.BLOCK * (nf - 1) + pl) if nf else
+                                          np.arange(pl) + 1, kv_start, page_row, page_size)
+        return out, n
+    m.build_positions = build_positions
+
+
+def _m_page_row_of_first_request(m):
+    orig = m.decode
+    def decode(*a, **kw):
+        if kw.get("page_table") is not None:
+            pt = np.asarray(kw["page_table"])
+            kw["page_table"] = np.repeat(pt[:1], pt.shape[0], axis=0)
+        return orig(*a, **kw)
+    m.decode = decode
+
+
+def _m_kv_scales_ignored(m):
+    orig = m.decode
+    def decode(*a, **kw):
+        a = list(a)
+        if len(a) > 11 and a[10] is not None:
+            a[10], a[11] = np.ones_like(a[10]), np.ones_like(a[11])
+        for key in ("k_scale", "v_scale"):
+            if kw.get(key) is not None:
+                kw[key] = np.ones_like(kw[key])
+        return orig(*a, **kw)
+    m.decode = decode
+
+
 MUTANTS = [_m_tie_higher_index, _m_unsorted_output, _m_bottom_k, _m_drop_partial, _m_no_kv_offset,
            _m_all_queries_full_length, _m_causal_off_by_one, _m_ignore_scale, _m_gqa_modulo,
            _m_fp8_bias8, _m_fp8_no_subnormals, _m_swap_kv_scales, _m_score_sign, _m_score_in_bf16,
            _m_ignore_blk_start, _m_sel_pad_keeps_k, _m_page_no_scale, _m_reuse_keeps_all,
-           _m_compress_truncate, _m_compress_ties_away, _m_compress_first_block_off]
+           _m_compress_truncate, _m_compress_ties_away, _m_compress_first_block_off, _m_v_from_k,
+           _m_softmax_unnormalised, _m_block_index_not_scaled, _m_partial_block_from_block_start,
+           _m_page_row_of_first_request, _m_kv_scales_ignored]
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda f: f.__name__[3:])
