@@ -314,6 +314,32 @@ def test_build_index_bit_exact():
     assert np.array_equal(n_pos.cpu().numpy(), ref["n_pos"])
 
 
+def test_decode_max_requests():
+    """The largest batch the ABI takes: 16,384 requests (40,573 queries) of 1-64
+    tokens, 24 of them long enough to need selection.  Grids reach 40,573
+    workgroups and the request lookup its deepest search; a sample of queries
+    (every query of the long rows, the first and last, and 300 others) is
+    checked against the oracle."""
+    need_gpu()
+    rng = np.random.default_rng(77)
+    R = 16384
+    lens = rng.integers(1, 65, R)
+    long_req = rng.choice(R, 24, replace=False)
+    lens[long_req] = rng.integers(2100, 6000, 24)
+    nq = np.minimum(rng.integers(1, 5, R), lens)
+    w = make_custom("maxreq", lens.tolist(), nq.tolist(), 2, 1, kv_dtype="bf16", seed=78, index_values="normal")
+    assert w.num_req == 16384          # QSA_MAX_REQUESTS
+    say("max requests", w.num_req, "queries", w.num_q)
+    got = run_decode(w)
+    qs = set(int(x) for x in rng.choice(w.num_q, 300, replace=False)) | {0, w.num_q - 1}
+    for r in long_req:
+        qs |= set(range(int(w.q_start[r]), int(w.q_start[r + 1])))
+    qs = sorted(qs)
+    ref = oracle_decode(w, want_scores=False, queries=qs)
+    assert_selection_equal(got, ref, queries=qs)
+    assert_out_close(got["out"], ref["out"], queries=qs)
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
 def test_ragged_batch_many_kv_heads(kv):
     """A batch of several requests whose (query, KV head) units stay under 512
