@@ -314,6 +314,20 @@ def test_build_index_bit_exact():
     assert np.array_equal(n_pos.cpu().numpy(), ref["n_pos"])
 
 
+def test_decode_max_blocks():
+    """The longest row the ABI takes: one request of 4,194,304 tokens, so its
+    last verify query has 2^20 full blocks (QSA_MAX_BLOCKS) and the selection
+    runs on 16,384-block slices and a 32,768-entry candidate row; FP8 KV."""
+    need_gpu()
+    w = make_custom("max-blocks", [4 * (1 << 20)], [4], 4, 1, kv_dtype="fp8_e4m3", seed=79, index_values="normal")
+    assert int(w.seq_len[0]) // 4 == 1 << 20
+    say("max blocks", int(w.seq_len[0]) // 4)
+    ref = oracle_decode(w, want_scores=False)
+    got = run_decode(w)
+    assert_selection_equal(got, ref)
+    assert_out_close(got["out"], ref["out"])
+
+
 def test_decode_max_requests():
     """The largest batch the ABI takes: 16,384 requests (40,573 queries) of 1-64
     tokens, 24 of them long enough to need selection.  Grids reach 40,573
