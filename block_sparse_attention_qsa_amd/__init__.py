@@ -285,6 +285,8 @@ def qsa_sparse_attn(batch: Batch, q, k_cache, v_cache, pos, n_pos, out, *, k_sca
     _dev(q, "q", _BF16)
     kv = _kv_args(k_cache, v_cache, k_scale, v_scale, hkv)
     _dev(pos, "pos", (torch.int32,))
+    if pos.dim() != 2 or pos.shape[0] != batch.num_q:
+        raise QsaError("pos must be [num_q, width]")
     _dev(n_pos, "n_pos", (torch.int32,), (batch.num_q,))
     _dev(out, "out", (torch.float32, torch.bfloat16), (batch.num_q, hq, HEAD_DIM))
     sm = 1.0 / math.sqrt(HEAD_DIM) if sm_scale is None else float(sm_scale)
@@ -299,6 +301,8 @@ def qsa_decode(batch: Batch, idx_q, ckeys, q, k_cache, v_cache, out, workspace, 
                stream=None) -> None:
     _dev(idx_q, "idx_q", _BF16, (batch.num_q, INDEX_DIM))
     _dev(ckeys, "ckeys", _BF16)
+    if ckeys.dim() != 2 or ckeys.shape[1] != INDEX_DIM:
+        raise QsaError("ckeys must be [rows, 128]")
     if q.dim() != 3 or q.shape[0] != batch.num_q or q.shape[2] != HEAD_DIM:
         raise QsaError("q must be [num_q, Hq, 128]")
     hq, hkv = int(q.shape[1]), int(k_cache.shape[1])
@@ -329,6 +333,8 @@ def qsa_decode_static(batch: Batch, idx_q, ckeys, q, k_cache, v_cache, out, *, k
     argument; see qsa.h for its size limit and sharing rules)."""
     _dev(idx_q, "idx_q", _BF16, (batch.num_q, INDEX_DIM))
     _dev(ckeys, "ckeys", _BF16)
+    if ckeys.dim() != 2 or ckeys.shape[1] != INDEX_DIM:
+        raise QsaError("ckeys must be [rows, 128]")
     if q.dim() != 3 or q.shape[0] != batch.num_q or q.shape[2] != HEAD_DIM:
         raise QsaError("q must be [num_q, Hq, 128]")
     hq, hkv = int(q.shape[1]), int(k_cache.shape[1])

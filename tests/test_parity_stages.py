@@ -314,6 +314,30 @@ def test_build_index_bit_exact():
     assert np.array_equal(n_pos.cpu().numpy(), ref["n_pos"])
 
 
+def test_binding_rejects_wrong_shapes():
+    """The binding refuses device tensors of the wrong shape before any call
+    into the library: position rows other than num_q, key rows other than 128
+    wide."""
+    need_gpu()
+    w = make_custom("shapes", [3000, 700], [2, 1], 16, 2, seed=215)
+    dev = upload(w)
+    b = batch_of(w)
+    out = torch.empty((w.num_q, 16, 128), dtype=torch.float32, device="cuda")
+    ws = qsa.alloc_workspace(b, 16, 2)
+    short_pos = torch.zeros((w.num_q - 1, qsa.WIDTH), dtype=torch.int32, device="cuda")
+    n_pos = torch.ones((w.num_q,), dtype=torch.int32, device="cuda")
+    with pytest.raises(qsa.QsaError, match="pos must be"):
+        qsa.qsa_sparse_attn(b, dev["q"], dev["k_cache"], dev["v_cache"], short_pos, n_pos, out, sm_scale=SM_SCALE,
+                            workspace=ws)
+    flat_keys = dev["ckeys"].reshape(-1)
+    for call in (lambda: qsa.qsa_decode(b, dev["idx_q"], flat_keys, dev["q"], dev["k_cache"], dev["v_cache"], out,
+                                        ws, sm_scale=SM_SCALE),
+                 lambda: qsa.qsa_decode_static(b, dev["idx_q"], flat_keys, dev["q"], dev["k_cache"],
+                                               dev["v_cache"], out, sm_scale=SM_SCALE)):
+        with pytest.raises(qsa.QsaError, match="ckeys must be"):
+            call()
+
+
 def test_decode_max_blocks():
     """The longest row the ABI takes: one request of 4,194,304 tokens, so its
     last verify query has 2^20 full blocks (QSA_MAX_BLOCKS) and the selection
